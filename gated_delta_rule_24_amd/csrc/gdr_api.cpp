@@ -1,0 +1,150 @@
+// C ABI of libgdr: argument validation, kernel selection and launch on the
+// caller's stream.  Declarations and the contract are in include/gdr.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "gdr_launch.h"
+
+namespace {
+
+constexpr uint32_t kKnownFlags = GDR_ACT_F32 | GDR_OUT_BF16 | GDR_ALPHA_SCALAR | GDR_B_SCALAR |
+                                 GDR_W_SCALAR;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_size_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Lazily checks, per device, that the current device is a gfx950.
+gdr_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GDR_ERR_DEVICE;
+    static std::mutex mu;
+    static int known[64];  // 0 unknown, 1 ok, 2 bad
+    if (dev >= 64) return GDR_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDR_ERR_DEVICE;
+        known[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    return known[dev] == 1 ? GDR_OK : GDR_ERR_DEVICE;
+}
+
+gdr_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return GDR_OK;
+    if (e == hipErrorInvalidValue) return GDR_ERR_UNSUPPORTED;
+    return GDR_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char* gdr_status_string(gdr_status s) {
+    switch (s) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_INVALID_ARG: return "invalid argument";
+        case GDR_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
+        case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDR_ERR_LAUNCH: return "kernel launch failed";
+        case GDR_ERR_DEVICE: return "no usable gfx950 device";
+    }
+    return "unknown status";
+}
+
+gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const void* b, const void* w, const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int d_k, int d_v, int chunk, uint32_t flags,
+                         void* stream) {
+    if (flags & ~kKnownFlags) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
+    if (!(chunk == 16 || chunk == 32 || chunk == 64)) return GDR_ERR_INVALID_ARG;
+    if (T % chunk != 0) return GDR_ERR_INVALID_ARG;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * T > (1LL << 40)) return GDR_ERR_INVALID_ARG;
+    if (!gdr::fwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+
+    gdr::FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
+    p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr;
+    p.BH = B * H; p.T = T; p.flags = flags;
+    int used = 0;
+    return from_hip(gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used));
+}
+
+gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const void* b, const void* w, float* S, void* o, int N, int H,
+                           int d_k, int d_v, uint32_t flags, void* stream) {
+    if (flags & ~kKnownFlags) return GDR_ERR_INVALID_ARG;
+    if (N < 1 || H < 1) return GDR_ERR_INVALID_ARG;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !log_alpha || !b || !w || !S || !o) return GDR_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S, o};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    if ((long long)N * H > (1LL << 31) - 1) return GDR_ERR_INVALID_ARG;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+
+    gdr::DecodeParams p;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w; p.S = S; p.o = o;
+    p.NH = (long long)N * H; p.flags = flags;
+    return from_hip(gdr::launch_decode(p, d_k, d_v, (hipStream_t)stream));
+}
+
+size_t gdr_chunk_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                     uint32_t flags) {
+    if (B < 1 || H < 1 || T < 0 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
+    if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return 0;
+    return gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
+}
+
+gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const void* b, const void* w, const float* S0, const void* dO,
+                         const float* dS_final, float* dq, float* dk, float* dv,
+                         float* dlog_alpha, float* db, float* dw, float* dS0, int B, int H,
+                         int T, int d_k, int d_v, int chunk, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (flags & ~(kKnownFlags & ~GDR_OUT_BF16)) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
+    if (!(chunk == 16 || chunk == 32 || chunk == 64)) return GDR_ERR_INVALID_ARG;
+    if (T % chunk != 0) return GDR_ERR_INVALID_ARG;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv ||
+                  !dlog_alpha || !db || !dw))
+        return GDR_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv,
+                          dlog_alpha, db, dw, dS0, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
+    const size_t need = gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+
+    gdr::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w; p.S0 = S0;
+    p.dO = dO; p.dSf = dS_final;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dla = dlog_alpha; p.db = db; p.dw = dw; p.dS0 = dS0;
+    p.states = nullptr; p.dstates = nullptr;
+    p.BH = B * H; p.T = T; p.flags = flags;
+    if (need > 0) {
+        const size_t half = need / 2;
+        p.states = reinterpret_cast<float*>(workspace);
+        p.dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + half);
+    }
+    return from_hip(gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI layer (gdr_api.cpp) and the kernel
+// translation units.  Not installed; callers use include/gdr.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const void* b;
+    const void* w;
+    float* S;
+    void* o;
+    long long NH;          // N * H
+    uint32_t flags;
+};
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const void* b;
+    const void* w;
+    const float* S0;       // may be null
+    void* o;               // may be null (state-only passes)
+    float* Sf;             // may be null
+    float* states;         // optional: chunk-start states [BH][NC][DK][DV] (backward recompute)
+    int BH;
+    int T;
+    uint32_t flags;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int dk, int dv, hipStream_t st);
+
+// Returns hipErrorInvalidValue for an unsupported (dk, dv, chunk, dtype).
+// *chunk_used receives the chunk size the kernel blocks with.
+hipError_t launch_fwd(const FwdParams& p, int dk, int dv, int chunk, hipStream_t st,
+                      int* chunk_used);
+bool fwd_supported(int dk, int dv, int chunk, uint32_t flags);
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const void* b;
+    const void* w;
+    const float* S0;
+    const void* dO;
+    const float* dSf;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dla;
+    float* db;
+    float* dw;
+    float* dS0;
+    float* states;         // workspace: chunk-start states
+    float* dstates;        // workspace: state gradients at chunk ends
+    int BH;
+    int T;
+    uint32_t flags;
+};
+
+size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
+bool bwd_supported(int dk, int dv, int chunk, uint32_t flags);
+hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t st);
+
+}  // namespace gdr

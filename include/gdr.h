@@ -1,0 +1,163 @@
+/*
+ * libgdr — gated delta rule kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Gated Delta Rule-2; Gated DeltaNet-2 Q&A page "Gated
+ * DeltaNet-2 — decoupling erase and write in linear attention", Q3, and
+ * "Gated DeltaNet-2 Review" §3-1), per independent (batch, head) pair:
+ *
+ *     S_t = (I - k_t (b_t ⊙ k_t)^T) D_t S_{t-1} + k_t (w_t ⊙ v_t)^T
+ *     D_t = diag(alpha_t),  alpha_t = exp(log_alpha_t)
+ *     o_t = S_t^T q_t                  (read-out after the write; "Gated
+ *                                       DeltaNet" explainer, mechanism)
+ *
+ * S_t is d_k x d_v.  b_t in R^{d_k} is the key-side erase gate, w_t in
+ * R^{d_v} the value-side write gate.  Tying b = w = beta·1 gives KDA; also
+ * making D_t = alpha_t·I gives Gated DeltaNet (Q&A page Q3).  Gates are
+ * neither clamped nor assumed to lie in [0,1]; the expanded erase range
+ * [0,2] ("Gated DeltaNet-2 Review" §5 ablation; sungsoo commentary, state
+ * tracking) works unchanged.  No query scaling and no normalisation of q, k
+ * is applied: that is the caller's job.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *   library never allocates device memory, never frees caller memory, and
+ *   keeps no state besides a lazily cached device-property record.
+ * - Execution is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL is the default stream).  No call synchronises.
+ * - Arguments are validated before any launch.  An invalid argument returns
+ *   a status and launches nothing.  Launch failures return GDR_ERR_LAUNCH.
+ *   No exception, abort or exit crosses the ABI.
+ * - Layouts are contiguous row-major.  "act" is the activation dtype chosen
+ *   by flags (bf16 bit patterns as uint16, or fp32).  Pointers must be
+ *   16-byte aligned.
+ * - Gate modes (flags): each of log_alpha, b, w is either per channel
+ *   ([..., d_k] / [..., d_k] / [..., d_v]) or one scalar per token ([...]).
+ *   Gated DeltaNet passes scalar log_alpha and the same scalar buffer as b
+ *   and w; KDA passes channel log_alpha and one scalar buffer as b and w;
+ *   the b-only / w-only ablations ("Gated DeltaNet-2 Review" §5 gate
+ *   ablation) are mixed modes.
+ * - Precision: with bf16 activations the dense chunk contractions run on
+ *   MFMA with f16 operands and fp32 accumulation; the state, log-decay and
+ *   the cumulative decay stay fp32 (the log-decay path runs in fp32:
+ *   "Gated DeltaNet-2 Review" §3-2 item 2).  With fp32 activations every
+ *   contraction runs on fp32 MFMA.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misalignment, T % chunk != 0 */
+    GDR_ERR_UNSUPPORTED = 2,     /* a valid request this build has no kernel for      */
+    GDR_ERR_WORKSPACE = 3,       /* workspace pointer NULL or smaller than required   */
+    GDR_ERR_LAUNCH = 4,          /* the HIP runtime rejected a launch                 */
+    GDR_ERR_DEVICE = 5           /* no usable gfx950 device / device query failed     */
+} gdr_status;
+
+/* flags (bitwise OR) */
+#define GDR_ACT_BF16      0x0u   /* q, k, v, b, w, dO are bf16 (uint16 bit patterns)  */
+#define GDR_ACT_F32       0x1u   /* q, k, v, b, w, dO are fp32                        */
+#define GDR_OUT_BF16      0x2u   /* o is bf16 (default fp32).  Forward/decode only.   */
+#define GDR_ALPHA_SCALAR  0x4u   /* log_alpha is one fp32 per token                   */
+#define GDR_B_SCALAR      0x8u   /* b is one value per token                          */
+#define GDR_W_SCALAR      0x10u  /* w is one value per token                          */
+
+#define GDR_ABI_VERSION 1
+
+int gdr_abi_version(void);
+const char* gdr_status_string(gdr_status s);
+
+/*
+ * Chunkwise-parallel forward (the WY form: in-chunk cumulative log-decay is
+ * absorbed into the rank-one erase factor, giving an asymmetric delta
+ * recurrence solved per chunk; Q&A page Q4, "Gated DeltaNet-2 Review"
+ * §3-2 item 5).
+ *
+ *   q, k       : act  [B, H, T, d_k]
+ *   v          : act  [B, H, T, d_v]
+ *   log_alpha  : fp32 [B, H, T, d_k]   or [B, H, T] with GDR_ALPHA_SCALAR
+ *   b          : act  [B, H, T, d_k]   or [B, H, T] with GDR_B_SCALAR
+ *   w          : act  [B, H, T, d_v]   or [B, H, T] with GDR_W_SCALAR
+ *   S0         : fp32 [B, H, d_k, d_v] initial state; NULL means zeros
+ *   o          : fp32 (or bf16 with GDR_OUT_BF16) [B, H, T, d_v], written
+ *   S_final    : fp32 [B, H, d_k, d_v], written; NULL means not written.
+ *                May alias S0 (each workgroup reads its block of S0 before
+ *                writing the same block).  No other aliasing is allowed.
+ *   chunk      : 16, 32 or 64; T must be a multiple of chunk.  The chunk is
+ *                a blocking choice: results equal the token recurrence up to
+ *                rounding for every chunk size.
+ * Supported: d_k, d_v in {16, 32, 64, 128}; B*H >= 1; T >= 0 (T == 0 copies
+ * S0 to S_final).  Returns GDR_ERR_UNSUPPORTED for other head sizes.
+ */
+gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* log_alpha, const void* b, const void* w,
+                         const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int d_k, int d_v, int chunk,
+                         uint32_t flags, void* stream);
+
+/*
+ * One recurrent decode step for N independent sequences (constant memory:
+ * the state is updated in place; Q&A page introduction, "Gated DeltaNet-2
+ * Review" §3-2 item 1).  Each (n, h) state is read once and written once.
+ *
+ *   q, k       : act  [N, H, d_k]
+ *   v          : act  [N, H, d_v]
+ *   log_alpha  : fp32 [N, H, d_k] or [N, H] with GDR_ALPHA_SCALAR
+ *   b          : act  [N, H, d_k] or [N, H] with GDR_B_SCALAR
+ *   w          : act  [N, H, d_v] or [N, H] with GDR_W_SCALAR
+ *   S          : fp32 [N, H, d_k, d_v], read and overwritten with S_t
+ *   o          : fp32 (or bf16) [N, H, d_v], written
+ * Supported: d_k, d_v in {16, 32, 64, 128}.  All arithmetic is fp32.
+ */
+gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* b, const void* w,
+                           float* S, void* o, int N, int H, int d_k, int d_v,
+                           uint32_t flags, void* stream);
+
+/*
+ * Gate-aware backward of gdr_chunk_fwd for the loss
+ *     L = <dO, o> + <dS_final, S_final>,
+ * with the erase-side gate gradient (db) and the write-side one (dw)
+ * accumulated separately (Q&A page Q4).
+ *
+ *   inputs as gdr_chunk_fwd, plus
+ *   dO         : act  [B, H, T, d_v]
+ *   dS_final   : fp32 [B, H, d_k, d_v]; NULL means zero
+ *   outputs (fp32, written, never accumulated into):
+ *   dq, dk     : [B, H, T, d_k]       dv : [B, H, T, d_v]
+ *   dlog_alpha : [B, H, T, d_k] (or [B, H, T] in scalar mode: the sum over
+ *                channels)
+ *   db         : [B, H, T, d_k] (or [B, H, T])   dw : [B, H, T, d_v] (or [B, H, T])
+ *                When b and w are the same scalar buffer (tied gates), the
+ *                gradient of that buffer is db + dw.
+ *   dS0        : [B, H, d_k, d_v]; may be NULL when not needed.
+ *   workspace  : device scratch of at least gdr_chunk_bwd_workspace_bytes()
+ *                bytes, owned by the caller; contents on entry are ignored.
+ * Supported: bf16 or fp32 activations, d_k = d_v = 128 or 64, chunk 64 or
+ * 32.  Returns GDR_ERR_UNSUPPORTED otherwise.
+ */
+size_t gdr_chunk_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v,
+                                     int chunk, uint32_t flags);
+
+gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v,
+                         const float* log_alpha, const void* b, const void* w,
+                         const float* S0, const void* dO, const float* dS_final,
+                         float* dq, float* dk, float* dv, float* dlog_alpha,
+                         float* db, float* dw, float* dS0,
+                         int B, int H, int T, int d_k, int d_v, int chunk,
+                         uint32_t flags, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,93 @@
+"""The C ABI library: it loads, exports every function include/gdr.h
+declares, and rejects invalid arguments before touching a device (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "gdr.h")
+
+
+def _lib():
+    import gated_delta_rule_24_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        import gated_delta_rule_24_amd.build as b
+        b.build(verbose=False)
+    return g.lib()
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_bwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    import gated_delta_rule_24_amd as g
+    assert set(declared_functions()) == set(g.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib()
+    assert lib.gdr_abi_version() == 1
+    for s in range(6):
+        assert len(lib.gdr_status_string(s)) > 0
+    assert lib.gdr_status_string(99) == b"unknown status"
+
+
+A = ctypes.c_void_p(0x10000)      # aligned fake pointer: never dereferenced
+MIS = ctypes.c_void_p(0x10004)    # misaligned
+
+
+def _fwd(lib, **kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, Sf=None, B=1, H=1, T=64, dk=128,
+                dv=128, chunk=64, flags=0)
+    args.update(kw)
+    return lib.gdr_chunk_fwd(args["q"], args["k"], args["v"], args["la"], args["b"], args["w"],
+                             args["S0"], args["o"], args["Sf"], args["B"], args["H"], args["T"],
+                             args["dk"], args["dv"], args["chunk"], args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(w=None), 1),
+    (dict(chunk=48), 1), (dict(T=100), 1), (dict(B=0), 1), (dict(T=-64), 1),
+    (dict(flags=0x100), 1), (dict(k=MIS), 1), (dict(Sf=MIS), 1),
+    (dict(dk=96), 2), (dict(dv=256), 2), (dict(dk=16, dv=128), 2),
+])
+def test_fwd_argument_validation(kw, status):
+    assert _fwd(_lib(), **kw) == status
+
+
+def test_decode_argument_validation():
+    lib = _lib()
+    ok = dict(q=A, k=A, v=A, la=A, b=A, w=A, S=A, o=A, N=4, H=2, dk=128, dv=128, flags=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.gdr_decode_step(a["q"], a["k"], a["v"], a["la"], a["b"], a["w"], a["S"],
+                                   a["o"], a["N"], a["H"], a["dk"], a["dv"], a["flags"], None)
+    assert call(S=None) == 1
+    assert call(N=0) == 1
+    assert call(o=MIS) == 1
+    assert call(flags=0x40) == 1
+    assert call(dk=48) == 2
+
+
+def test_bwd_workspace_query_and_validation():
+    lib = _lib()
+    n = lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0)
+    assert n == 0 or n >= 2 * 2 * 2 * 128 * 128 * 4
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 48, 0) == 0

@@ -1,0 +1,187 @@
+"""GPU parity of gdr_chunk_fwd against the fp64 token-recurrence oracle.
+
+Tolerances (max|Δ|/rms(ref) over the whole tensor, separately for o and
+S_final): 1e-4 with fp32 activations, 2e-2 with bf16 q/k/v/b/w (fp32 state
+and decay).  Sizes span several chunks and every gate mode; the full
+workloads are checked on sampled heads, whose oracle finishes in seconds."""
+import numpy as np
+import pytest
+
+import gdr_synth as gs
+from tests.helpers import flat_heads, oracle_fwd, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, chunk=None, S0=None, out_dtype=None, return_state=True):
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    d = to_dev(inp)
+    s0 = d["S0"] if S0 is None else S0
+    o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], s0,
+                          chunk=chunk or inp.chunk, out_dtype=out_dtype or torch.float32,
+                          return_state=return_state)
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def _check(inp, o, sf, tol, heads=None):
+    o_ref, s_ref = oracle_fwd(inp, heads=heads)
+    o_g = flat_heads(o.float().cpu().numpy(), inp.B, inp.H, heads)
+    s_g = flat_heads(sf.cpu().numpy(), inp.B, inp.H, heads)
+    eo, es = rel_err(o_g, o_ref), rel_err(s_g, s_ref)
+    print(f"  err o={eo:.3e} S={es:.3e} (tol {tol})", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+def _case(name, **kw):
+    print(f"fwd case {name} {kw}", flush=True)
+    return gs.preset(name, **kw) if name in gs.PRESETS else gs.make_inputs(**kw)
+
+
+def test_tiny_gdn_fp32():
+    inp = _case("gdn_tiny")
+    o, sf = _run(inp)
+    _check(inp, o, sf, 1e-4)
+
+
+SMALL = [
+    # name, kwargs, tol
+    ("gdn2_bf16_c64", dict(B=2, H=2, T=320, dk=128, dv=128, chunk=64), 2e-2),
+    ("gdn2_bf16_c32", dict(B=1, H=2, T=256, dk=128, dv=128, chunk=32), 2e-2),
+    ("gdn2_bf16_c16", dict(B=1, H=2, T=128, dk=128, dv=128, chunk=16), 2e-2),
+    ("gdn_scalar_bf16", dict(B=2, H=2, T=256, dk=128, dv=128, alpha_mode="scalar", b_mode="scalar",
+                             w_mode="scalar", tied=True, s0_std=None), 2e-2),
+    ("kda_bf16", dict(B=1, H=3, T=192, dk=128, dv=128, b_mode="scalar", w_mode="scalar",
+                      tied=True), 2e-2),
+    ("b_only_channel", dict(B=1, H=2, T=192, dk=64, dv=64, w_mode="scalar"), 2e-2),
+    ("w_only_channel", dict(B=1, H=2, T=192, dk=64, dv=64, b_mode="scalar"), 2e-2),
+    ("d64_c64", dict(B=2, H=2, T=256, dk=64, dv=64), 2e-2),
+    ("d32_c32", dict(B=2, H=2, T=160, dk=32, dv=32, chunk=32), 2e-2),
+    ("d16_c16", dict(B=2, H=2, T=96, dk=16, dv=16, chunk=16), 2e-2),
+    ("dk64_dv128", dict(B=1, H=2, T=192, dk=64, dv=128), 2e-2),
+    ("dk128_dv64", dict(B=1, H=2, T=192, dk=128, dv=64), 2e-2),
+    ("erase_range_0_2", dict(B=1, H=2, T=256, dk=128, dv=128, gate_hi=2.0), 2e-2),
+    ("f32_d128_c64", dict(B=1, H=2, T=256, dk=128, dv=128, act="f32"), 1e-4),
+    ("f32_d128_c32", dict(B=1, H=2, T=160, dk=128, dv=128, act="f32", chunk=32), 1e-4),
+    ("f32_d64_c64", dict(B=1, H=2, T=192, dk=64, dv=64, act="f32"), 1e-4),
+    ("f32_d32_c64", dict(B=2, H=2, T=192, dk=32, dv=32, act="f32"), 1e-4),
+    ("f32_dk128_dv64", dict(B=1, H=2, T=128, dk=128, dv=64, act="f32", chunk=32), 1e-4),
+    ("f32_scalar_gdn", dict(B=1, H=2, T=128, dk=128, dv=128, act="f32", alpha_mode="scalar",
+                            b_mode="scalar", w_mode="scalar", tied=True), 1e-4),
+    ("f32_strong_decay", dict(B=1, H=2, T=128, dk=64, dv=64, act="f32", chunk=32,
+                              decay_scale=0.5), 1e-4),
+    ("bf16_strong_decay_c16", dict(B=1, H=2, T=128, dk=64, dv=64, chunk=16, decay_scale=0.5), 2e-2),
+]
+
+
+@pytest.mark.parametrize("name,kw,tol", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases(name, kw, tol):
+    inp = _case(name, **kw)
+    o, sf = _run(inp)
+    _check(inp, o, sf, tol)
+
+
+def test_zero_initial_state_pointer_equals_zeros():
+    import torch
+    inp = _case("s0_none", B=1, H=2, T=128, dk=128, dv=128, s0_std=None)
+    o1, s1 = _run(inp)
+    z = torch.zeros((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+    o2, s2 = _run(inp, S0=z)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    _check(inp, o1, s1, 2e-2)
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    import torch
+    inp = _case("bf16_out", B=1, H=2, T=192, dk=128, dv=128)
+    o32, s32 = _run(inp)
+    o16, s16 = _run(inp, out_dtype=torch.bfloat16)
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert torch.equal(s32, s16)
+
+
+def test_state_may_alias_initial_state():
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    inp = _case("alias", B=2, H=2, T=128, dk=128, dv=128)
+    o_ref, s_ref = _run(inp)
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    o = torch.empty_like(o_ref)
+    gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S, o, S,
+                      2, 2, 128, 128, 128, 64, gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"]))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, s_ref)
+
+
+def test_empty_sequence_copies_state():
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    S0 = torch.randn(2, 3, 64, 64, device="cuda")
+    Sf = torch.full_like(S0, 7.0)
+    e = torch.empty(0, device="cuda", dtype=torch.bfloat16)
+    o = torch.empty(0, device="cuda")
+    gdr.gdr_chunk_fwd(e, e, e, o, e, e, S0, o, Sf, 2, 3, 0, 64, 64, 64, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(Sf, S0)
+
+
+def test_deterministic_bitwise():
+    import torch
+    inp = _case("det", B=2, H=2, T=256, dk=128, dv=128)
+    o1, s1 = _run(inp)
+    o2, s2 = _run(inp)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_chunk_size_invariance():
+    inp = _case("chunks", B=1, H=2, T=256, dk=128, dv=128)
+    outs = {c: _run(inp, chunk=c) for c in (16, 32, 64)}
+    for c, (o, sf) in outs.items():
+        _check(inp, o, sf, 2e-2)
+    o64 = outs[64][0].cpu().numpy()
+    for c in (16, 32):
+        assert rel_err(outs[c][0].cpu().numpy(), o64) <= 2e-2
+
+
+def test_split_sequence_continuity():
+    """fwd(T) equals fwd(T1) followed by fwd(T - T1) starting from its state."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    inp = _case("split", B=1, H=2, T=256, dk=128, dv=128)
+    d = to_dev(inp)
+    o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+    h = lambda t: t[:, :, :128].contiguous()
+    t2 = lambda t: t[:, :, 128:].contiguous()
+    o1, s1 = gdr.chunk_fwd(*(h(d[n]) for n in ("q", "k", "v", "log_alpha", "b", "w")), d["S0"])
+    o2, s2 = gdr.chunk_fwd(*(t2(d[n]) for n in ("q", "k", "v", "log_alpha", "b", "w")), s1)
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat([o1, o2], 2).cpu().numpy(), o.cpu().numpy()) <= 1e-5
+    assert rel_err(s2.cpu().numpy(), sf.cpu().numpy()) <= 1e-5
+
+
+def test_decay_beyond_f16_range_is_loud():
+    """A chunk whose accumulated decay exceeds the f16 operand range poisons
+    its head's outputs with NaN instead of returning wrong numbers."""
+    import torch
+    inp = _case("strong", B=1, H=2, T=128, dk=64, dv=64, decay_scale=2.0)
+    o, sf = _run(inp)
+    assert torch.isnan(sf).any()
+    assert torch.isnan(o[:, :, -1]).all()
+
+
+def test_gdn2_full_workload_sampled_heads():
+    """Gated DeltaNet-2 at B=2, H=16, T=8192, d=128, chunk 64 (the timed
+    launch), compared on 4 sampled heads."""
+    inp = _case("gdn2")
+    o, sf = _run(inp)
+    _check(inp, o, sf, 2e-2, heads=[0, 7, 21, 31])
+
+
+def test_gdn_full_workload_sampled_heads():
+    """Gated DeltaNet (scalar gates) at B=4, H=16, T=2048, d=128."""
+    inp = _case("gdn")
+    o, sf = _run(inp)
+    _check(inp, o, sf, 2e-2, heads=[0, 13, 40, 63])
