@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+Headline: the chunkwise Gated DeltaNet-2 forward (gate prep, intra-chunk WY,
+inter-chunk state pass and output, fused in one kernel) at B=2, H=16,
+T=8192, d_k=d_v=128, chunk 64, bf16 activations, fp32 log-decay and state.
+One step = one gdr_chunk_fwd call over that batch, inputs resident in HBM.
+value = B*H*T head-tokens per second of wall time over the timed steps.
+
+Also reported in the same JSON line: the recurrent decode step (256
+sequences x 32 heads, fp32 state streamed in place) in GB/s, the backward
+when the library supports it, the roofline position of the forward kernel
+(algorithmic HBM bytes per launch over the measured launch duration), and
+the fp64 CPU oracle timed on this host as a reference baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("tokens/s (B·H·T) GDN-2 chunk fwd T=8K d=128 bf16; % MFMA peak; "
+          "decode GB/s")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense f16/bf16 MFMA
+
+# forward workload
+FB, FH, FT, FD, FC = 2, 16, 8192, 128, 64
+# algorithmic HBM bytes per head-token: q,k,v bf16 + log_alpha fp32 + b,w bf16
+# + o fp32, plus S0 read and S_final written once per head
+FWD_BYTES_PER_TOKEN = 3 * FD * 2 + FD * 4 + 2 * FD * 2 + FD * 4
+FWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
+# dense MFMA work per head-token: W'S-type state products 6 d_k d_v and the
+# in-chunk products 2C(3 d_k + 2 d_v)
+FWD_FLOPS_PER_TOKEN = 6 * FD * FD + 2 * FC * (3 * FD + 2 * FD)
+
+# decode workload
+DN, DH, DD = 256, 32, 128
+DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + DD * 2) + DD * 4
+
+FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd.hip",
+                      "gated_delta_rule_24_amd/csrc/gdr_device.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from committed PMC counters, or None if
+    absent or taken on a different version of the kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    txt = open(TRAFFIC_SUMMARY).read()
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_h or not m_b or m_h.group(1) != source_hash(FWD_KERNEL_SOURCES):
+        return None
+    return float(m_b.group(1))
+
+
+def upload(inp):
+    import torch
+    act = torch.bfloat16 if inp.act == "bf16" else torch.float32
+    out = {}
+    for n, a in inp.arrays.items():
+        if a is None:
+            out[n] = None
+            continue
+        dt = torch.float32 if n in ("log_alpha", "S0") else act
+        out[n] = torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    if inp.arrays["b"] is inp.arrays["w"]:
+        out["w"] = out["b"]
+    return out
+
+
+def time_loop(fn, steps, warmup):
+    """Average wall ms and event ms per call over `steps` timed calls; the
+    events are recorded on torch's current stream, where libgdr launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def bench_fwd(steps, warmup):
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    inp = gs.preset("gdn2", seed=0)
+    d = upload(inp)
+    o = torch.empty((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((FB, FH, FD, FD), dtype=torch.float32, device="cuda")
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+
+    def step():
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], o, Sf,
+                          FB, FH, FT, FD, FD, FC, flags)
+    wall_ms, ev_ms = time_loop(step, steps, warmup)
+    return inp, wall_ms, ev_ms
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    S = torch.from_numpy(gs.decode_state(DN, DH, DD, DD, seed=0)).cuda()
+    toks = []
+    for st in range(8):
+        t = gs.decode_token(DN, DH, DD, DD, st, seed=0)
+        toks.append({n: torch.from_numpy(a).to(torch.float32 if n == "log_alpha"
+                                               else torch.bfloat16).cuda() for n, a in t.items()})
+    o = torch.empty((DN, DH, DD), dtype=torch.float32, device="cuda")
+    i = [0]
+
+    def step():
+        t = toks[i[0] % 8]
+        i[0] += 1
+        gdr.gdr_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["b"], t["w"], S, o,
+                            DN, DH, DD, DD, 0)
+    wall_ms, ev_ms = time_loop(step, steps, warmup)
+    return wall_ms, ev_ms
+
+
+def bench_copy(steps, warmup):
+    """Plain 1 GiB device copy, the calibration kernel for HBM counters."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    wall_ms, ev_ms = time_loop(lambda: dst.copy_(src), steps, warmup)
+    return wall_ms, ev_ms
+
+
+def cpu_baseline(inp):
+    """The fp64 oracle on this host over the same GDN-2 workload."""
+    import oracle
+    a = inp.arrays
+    sel = lambda x: x.reshape((FB * FH,) + x.shape[2:])
+    t0 = time.perf_counter()
+    oracle.fwd(sel(a["q"]), sel(a["k"]), sel(a["v"]), sel(a["log_alpha"]), sel(a["b"]),
+               sel(a["w"]), sel(a["S0"]))
+    dt = time.perf_counter() - t0
+    return dict(value=FB * FH * FT / dt, unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"full workload: all {FB * FH} heads x {FT} tokens, d=128, fp64 "
+                       f"token recurrence, OpenMP over heads ({dt:.1f} s wall)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+                    help="run one kernel only (for profiler runs); prints timings to stderr")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.only == "copy":
+        w, e = bench_copy(args.steps, args.warmup)
+        log(f"copy 1 GiB: {e:.3f} ms/launch, {2 * (1 << 30) / e / 1e6:.1f} GB/s")
+        return
+    if args.only == "decode":
+        w, e = bench_decode(args.steps, args.warmup)
+        log(f"decode: {e * 1e3:.1f} us/step, {DN * DH * DEC_BYTES_PER_HEAD / e / 1e6:.1f} GB/s")
+        return
+
+    inp, wall_ms, ev_ms = bench_fwd(args.steps, args.warmup)
+    ntok = FB * FH * FT
+    fwd_bytes = ntok * FWD_BYTES_PER_TOKEN + FB * FH * FWD_STATE_BYTES_PER_HEAD
+    fwd_flops = ntok * FWD_FLOPS_PER_TOKEN
+    achieved = fwd_bytes / (ev_ms * 1e-3) / 1e9
+    log(f"fwd: wall {wall_ms * 1e3:.1f} us/step, kernel {ev_ms * 1e3:.1f} us/launch, "
+        f"{achieved:.0f} GB/s, {fwd_flops / (ev_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    if args.only == "fwd":
+        return
+
+    dec_wall, dec_ev = bench_decode(max(args.steps, 10), args.warmup)
+    dec_gbs = DN * DH * DEC_BYTES_PER_HEAD / (dec_ev * 1e-3) / 1e9
+    log(f"decode: {dec_ev * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": ntok / (wall_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gdn2_chunk_fwd B=2 H=16 T=8192 d_k=d_v=128 chunk=64",
+            "B": FB, "H": FH, "T": FT, "d_k": FD, "d_v": FD, "chunk": FC,
+            "activations": "bf16", "mfma_operands": "f16", "accumulate": "f32",
+            "state": "f32", "log_decay": "f32", "o": "f32",
+            "gates": "channel log_alpha, channel b (erase), channel w (write)",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "mfma": {
+            "achieved": fwd_flops / (ev_ms * 1e-3) / 1e12,
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": fwd_flops / (ev_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "flops_per_launch": fwd_flops,
+        },
+        "fwd_kernel_us": ev_ms * 1e3,
+        "fwd_bytes_per_launch": fwd_bytes,
+        "decode": {
+            "workload": "decode N=256 H=32 d=128 fp32 state in place",
+            "us_per_step": dec_ev * 1e3,
+            "GB_per_s": dec_gbs,
+            "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
+            "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

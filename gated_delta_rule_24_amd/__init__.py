@@ -32,6 +32,7 @@ GDR_OUT_BF16 = 0x2
 GDR_ALPHA_SCALAR = 0x4
 GDR_B_SCALAR = 0x8
 GDR_W_SCALAR = 0x10
+GDR_FWD_GENERIC = 0x20
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "launch", 5: "device"}
 
@@ -158,7 +159,8 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_a
 
 
 def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
-              out_dtype=torch.float32, return_state: bool = True, stream=None):
+              out_dtype=torch.float32, return_state: bool = True, stream=None,
+              generic: bool = False):
     """q, k: [B,H,T,dk]; v: [B,H,T,dv]; log_alpha, b: [B,H,T,dk] or [B,H,T];
     w: [B,H,T,dv] or [B,H,T]; S0: [B,H,dk,dv] fp32 or None.
     Returns (o [B,H,T,dv], S_final [B,H,dk,dv] or None)."""
@@ -167,6 +169,8 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
     flags = gate_flags(q, log_alpha, b, w)
     if out_dtype == torch.bfloat16:
         flags |= GDR_OUT_BF16
+    if generic:
+        flags |= GDR_FWD_GENERIC
     o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
     Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
     gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, Sf, B, H, T, dk, dv, chunk, flags, stream)

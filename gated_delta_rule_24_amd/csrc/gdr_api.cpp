@@ -10,7 +10,7 @@
 namespace {
 
 constexpr uint32_t kKnownFlags = GDR_ACT_F32 | GDR_OUT_BF16 | GDR_ALPHA_SCALAR | GDR_B_SCALAR |
-                                 GDR_W_SCALAR;
+                                 GDR_W_SCALAR | GDR_FWD_GENERIC;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

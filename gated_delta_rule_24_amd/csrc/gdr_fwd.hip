@@ -97,14 +97,11 @@ __device__ __forceinline__ void st4<float>(float* p, floatx4 v) {
 template <bool F32>
 __device__ __forceinline__ Raw4<F32> load_gate(const void* base, size_t idx4, size_t idx1, bool scalar) {
     if (!scalar) return load_raw4<F32>(base, idx4);
+    // only element 0 is defined in scalar mode (cvt_gate broadcasts it); leaving the
+    // rest unwritten keeps VALU writes out of registers with loads in flight
     Raw4<F32> r;
-    if constexpr (F32) {
-        r.f[0] = reinterpret_cast<const float*>(base)[idx1];
-        r.f[1] = r.f[2] = r.f[3] = 0.f;
-    } else {
-        r.u.x = reinterpret_cast<const uint16_t*>(base)[idx1];
-        r.u.y = 0;
-    }
+    if constexpr (F32) r.f[0] = reinterpret_cast<const float*>(base)[idx1];
+    else r.u.x = reinterpret_cast<const uint16_t*>(base)[idx1];
     return r;
 }
 template <bool F32>
@@ -303,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
                 *reinterpret_cast<floatx4*>(sX + r * LDX + 4 * cqv) = x;
             }
         }
-        if (c + 1 < NC) issue_loads(c + 1);
+        issue_loads(c + 1 < NC ? c + 1 : c);   // unconditional: loads land in the carried registers
         if (__syncthreads_or(over)) poisoned = true;
 
         // ================= A, P (MFMA) and S' =================
@@ -539,6 +536,10 @@ bool fwd_supported(int dk, int dv, int chunk, uint32_t flags) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dk, int dv, int chunk, hipStream_t st, int* used) {
+    if (!(p.flags & GDR_FWD_GENERIC) && fwd_pipe_supported(dk, dv, chunk, p.flags)) {
+        if (used) *used = chunk;
+        return launch_fwd_pipe(p, dk, dv, st);
+    }
     if (dk == 16 && dv == 16) return launch_d<16, 16>(p, chunk, st, used);
     if (dk == 32 && dv == 32) return launch_d<32, 32>(p, chunk, st, used);
     if (dk == 64 && dv == 64) return launch_d<64, 64>(p, chunk, st, used);

@@ -1,0 +1,660 @@
+// Pipelined chunkwise forward of the gated delta rule (the fast path for
+// bf16 activations, chunk 64, d_k and d_v in {64, 128}).
+//
+// Same mathematics as the generic kernel (gdr_fwd.hip): per chunk,
+//   E = b⊙k⊙exp(g-g_C), Qs = q⊙exp(g-g_C), Kh = k⊙exp(g_C-g), X = w⊙v,
+//   A = strict_lower(E Kh^T), P = lower(Qs Kh^T), S' = diag(exp(g_C)) S,
+//   (I + A) U = X - E S',  O = Qs S' + P U,  S <- S' + Kh^T U
+// (decay absorbed into the rank-one erase factor; Gated DeltaNet-2 Q&A page
+// Q4 and "Gated DeltaNet-2 Review" §3-2 item 5).
+//
+// One workgroup of 12 waves per (batch·head, block of VB = 64 value
+// columns); two roles, two segments per chunk separated by workgroup
+// barriers:
+//   * 8 producer waves build the key-side operands of the NEXT chunk: the
+//     fp32 in-chunk prefix of the log-decay (wave shuffles), E, Qs, Kh, Kh^T
+//     and X^T.  This element-wise work (two exp2 per key element) is the
+//     VALU-bound part, so it is spread over both segments and overlaps all
+//     MFMA work.  Global loads are issued one chunk ahead, split so that each
+//     has at least a segment of slack, and the lines of the chunk after are
+//     touched (one dword per 128-byte line) so those loads hit L2.
+//   * 4 consumer waves each own a 16-column strip of the fp32 state (MFMA
+//     accumulators) and process the CURRENT chunk: segment 1 computes the
+//     A/P tiles (each wave also the diagonal A tile it then inverts by
+//     forward substitution in fp32); segment 2 runs the state chain in
+//     registers: Y = [E; Qs] S', U by blocked forward substitution
+//     U_k = T_kk (R_k - sum_{j<k} A_kj U_j), O = Qs S' + P U and the state
+//     update.
+// Operands produced for the next chunk are double-buffered in LDS; Kh^T is
+// written one chunk late into a single buffer.  f16 operands of the 16-wide
+// k-steps are placed by an XOR swizzle so producer row writes and consumer
+// fragment reads are both free of LDS bank conflicts.
+#include "gdr_device.h"
+#include "gdr_launch.h"
+
+namespace gdr {
+
+namespace pipe {
+
+constexpr int C = 64;
+constexpr int NPW = 8;                  // producer waves
+constexpr int NCW = 4;                  // consumer waves (VB = 64)
+constexpr int VB = 16 * NCW;
+constexpr float kDecayLimit = 10.0f;    // f16 operand range, as in the generic kernel
+constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// Element offset of (row, col) in a [C][DK] f16 array stored as 8-byte units
+// whose index is XORed with a function of the row.  Rows 4*rg + r (producer
+// writes, 8 consecutive rg) and rows n (consumer reads, 8 consecutive n) then
+// fall on distinct LDS banks, with no padding.  col must be a multiple of 4
+// for 8-byte accesses, of 8 for 16-byte ones.
+template <int DK>
+__device__ __forceinline__ int swz(int row, int col) {
+    constexpr int FM = DK >= 128 ? 7 : 3;
+    const int f = ((row ^ (row >> 2)) & FM) << 2;
+    return row * DK + (((col >> 2) ^ f) << 2) + (col & 3);
+}
+
+template <int DK>
+struct Layout {
+    static constexpr int LDC = C + 8;      // Kh^T and X^T rows (f16)
+    static constexpr int LDB = 20;         // packed 16x16 blocks (f16)
+    static constexpr int LDD = 20;         // transposed diagonal blocks of A (fp32)
+    static constexpr size_t szE = (size_t)C * DK * 2;
+    static constexpr size_t oE = 0;                                       // [2][C][DK] swizzled
+    static constexpr size_t oQ = align16(oE + 2 * szE);                   // [2][C][DK] swizzled
+    static constexpr size_t oKr = align16(oQ + 2 * szE);                  // [2][C][DK] swizzled
+    static constexpr size_t oKT = align16(oKr + 2 * szE);                 // [DK][LDC]
+    static constexpr size_t oXT = align16(oKT + (size_t)DK * LDC * 2);    // [2][VB][LDC]
+    static constexpr size_t oG = align16(oXT + 2 * (size_t)VB * LDC * 2); // [2][DK] fp32
+    static constexpr size_t oF = align16(oG + 2 * DK * 4);                // [2][NPW] int
+    static constexpr size_t oP = align16(oF + 2 * NPW * 4);               // [10][16][LDB]
+    static constexpr size_t oAn = align16(oP + 10 * 16 * LDB * 2);        // [6][16][LDB]
+    static constexpr size_t oTd = align16(oAn + 6 * 16 * LDB * 2);        // [4][16][LDB]
+    static constexpr size_t oAd = align16(oTd + 4 * 16 * LDB * 2);        // [4][16][LDD] fp32
+    static constexpr size_t bytes = align16(oAd + 4 * 16 * LDD * 4);
+};
+
+__device__ __forceinline__ int blkP(int mt, int nt) { return mt * (mt + 1) / 2 + nt; }
+__device__ __forceinline__ int blkA(int mt, int nt) { return mt * (mt - 1) / 2 + nt; }
+
+__device__ __forceinline__ half4 to_h4(floatx4 v) {
+    half4 h;
+    h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
+    return h;
+}
+__device__ __forceinline__ floatx4 from_h4(half4 h) {
+    floatx4 v;
+    v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
+    return v;
+}
+__device__ __forceinline__ half8 cat8(half4 a, half4 b) {
+    half8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+__device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
+__device__ __forceinline__ floatx4 mfma16(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma32(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 exp2v(floatx4 x) {
+    floatx4 r;
+    r[0] = __builtin_amdgcn_exp2f(x[0]); r[1] = __builtin_amdgcn_exp2f(x[1]);
+    r[2] = __builtin_amdgcn_exp2f(x[2]); r[3] = __builtin_amdgcn_exp2f(x[3]);
+    return r;
+}
+__device__ __forceinline__ floatx4 bf4(uint2 u) {
+    floatx4 f;
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
+    return f;
+}
+__device__ __forceinline__ floatx4 splat4(float x) {
+    floatx4 f;
+    f[0] = f[1] = f[2] = f[3] = x;
+    return f;
+}
+__device__ __forceinline__ floatx4 shfl_up4(floatx4 v, int d) {
+    floatx4 r;
+    r[0] = __shfl_up(v[0], d, 64); r[1] = __shfl_up(v[1], d, 64);
+    r[2] = __shfl_up(v[2], d, 64); r[3] = __shfl_up(v[3], d, 64);
+    return r;
+}
+__device__ __forceinline__ floatx4 shfl4(floatx4 v, int src) {
+    floatx4 r;
+    r[0] = __shfl(v[0], src, 64); r[1] = __shfl(v[1], src, 64);
+    r[2] = __shfl(v[2], src, 64); r[3] = __shfl(v[3], src, 64);
+    return r;
+}
+
+// AS / BS / WS: log_alpha / b / w given as one scalar per token.
+template <int DK, int DV, bool AS, bool BS, bool WS>
+__global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams p) {
+    using L = Layout<DK>;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    constexpr int NVB = DV / VB;
+    constexpr int NKT = DK / 16;            // channel tiles of the state
+    constexpr int NKS = DK / 32;            // 32-wide K steps over channels
+    // producer key-side mapping: wave pw owns DK/NPW channels; lane = (cql, rg)
+    constexpr int QPW = DK / (4 * NPW);     // channel quads per producer wave
+    constexpr int RGW = 64 / QPW;           // row groups per wave
+    constexpr int RPT = C / RGW;            // rows per lane
+    constexpr int RH = RPT / 2;             // rows per segment
+    // producer value-side mapping (X^T): VB/4 column quads x token groups
+    constexpr int XCQ = VB / 4;
+    constexpr int XTG = 64 * NPW / XCQ;
+    constexpr int XTT = C / XTG;            // tokens per lane
+    constexpr int LDC = L::LDC, LDB = L::LDB, LDD = L::LDD;
+    static_assert(RPT >= 2 && RPT % 2 == 0, "row split");
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    _Float16* sE = reinterpret_cast<_Float16*>(smem + L::oE);
+    _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::oQ);
+    _Float16* sKr = reinterpret_cast<_Float16*>(smem + L::oKr);
+    _Float16* sKT = reinterpret_cast<_Float16*>(smem + L::oKT);
+    _Float16* sXT = reinterpret_cast<_Float16*>(smem + L::oXT);
+    float* sGam = reinterpret_cast<float*>(smem + L::oG);
+    int* sFlag = reinterpret_cast<int*>(smem + L::oF);
+    _Float16* sP = reinterpret_cast<_Float16*>(smem + L::oP);
+    _Float16* sAn = reinterpret_cast<_Float16*>(smem + L::oAn);
+    _Float16* sTd = reinterpret_cast<_Float16*>(smem + L::oTd);
+    float* sAd = reinterpret_cast<float*>(smem + L::oAd);
+
+    // the wave index is uniform: keep it (and what derives from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const bool producer = wave >= NCW;
+    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lid / NVB, vb = lid % NVB;
+    const int Tn = p.T, NC = Tn / C;
+    const size_t tok0 = (size_t)bh * Tn;
+    const int n_l = lane & 15, g_l = lane >> 4;
+    const int m_l = 4 * g_l;
+
+    if (producer) {
+        // ======================================================== producer
+        const int pw = wave - NCW;
+        // lane-derived indices; reassigned from an opaque copy of the lane id each
+        // iteration so the compiler does not hoist (and spill) their derived addresses
+        int cql, rg, ch0, ptid, xcq, xtg;
+        auto set_lane = [&]() {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            cql = ln % QPW;
+            rg = ln / QPW;
+            ch0 = pw * (DK / NPW) + 4 * cql;
+            ptid = 64 * pw + ln;
+            xcq = ptid % XCQ;
+            xtg = ptid / XCQ;
+        };
+        set_lane();
+        const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q);
+        const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k);
+        const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b);
+        const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v);
+        const uint16_t* wg = reinterpret_cast<const uint16_t*>(p.w);
+
+        uint2 rq[RPT], rk[RPT], rb[RPT];
+        floatx4 rla[RPT];
+        uint2 rv[XTT], rw[XTT];
+        using KhVec = _Float16 __attribute__((ext_vector_type(RPT)));
+        KhVec khp[4];                       // Kh of the previous chunk (late Kh^T write)
+        floatx4 gl[RPT];                    // local inclusive prefix (log2 units)
+        floatx4 excl = zero4(), gC = zero4();
+        unsigned touch = 0;                 // keeps the L2 touch loads alive
+        uint32_t tpend[2] = {0u, 0u};       // touch values, folded in one iteration later
+
+        // global loads, by group: decay (all rows), q/k/b rows [r0, r1), v/w
+        auto ld_la = [&](int c) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const size_t t = tok0 + (size_t)c * C + rg * RPT + r;
+                if constexpr (AS) rla[r][0] = p.la[t];
+                else rla[r] = *reinterpret_cast<const floatx4*>(p.la + t * DK + ch0);
+            }
+        };
+        auto ld_qkb = [&](int c, int r0, int r1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                if (r < r0 || r >= r1) continue;
+                const size_t t = tok0 + (size_t)c * C + rg * RPT + r;
+                const size_t ix = t * DK + ch0;
+                rq[r] = *reinterpret_cast<const uint2*>(qg + ix);
+                rk[r] = *reinterpret_cast<const uint2*>(kg + ix);
+                if constexpr (BS) rb[r].x = bg[t];
+                else rb[r] = *reinterpret_cast<const uint2*>(bg + ix);
+            }
+        };
+        auto ld_vw = [&](int c) {
+#pragma unroll
+            for (int r = 0; r < XTT; ++r) {
+                const size_t t = tok0 + (size_t)c * C + xtg * XTT + r;
+                const size_t ix = t * DV + vb * VB + 4 * xcq;
+                rv[r] = *reinterpret_cast<const uint2*>(vg + ix);
+                if constexpr (WS) rw[r].x = wg[t];
+                else rw[r] = *reinterpret_cast<const uint2*>(wg + ix);
+            }
+        };
+        // one dword of each 128-byte line this workgroup will read for chunk c
+        auto touch_chunk = [&](int c) {
+            const size_t t0 = tok0 + (size_t)c * C;
+            constexpr int LK = C * DK * 2 / 128;                  // lines of q, k or b
+            constexpr int LA = AS ? C * 4 / 128 : C * DK * 4 / 128;
+            constexpr int LB = BS ? 1 : LK;
+            constexpr int LV = C;                                  // one 128-byte row segment per token
+            constexpr int LW = WS ? 1 : LV;
+            constexpr int NL = 2 * LK + LB + LA + LV + LW;
+            // fold the previous touches first: consuming a load right after issuing it
+            // would wait a full memory round trip
+            touch ^= tpend[0] ^ tpend[1];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int li = ptid + s2 * 64 * NPW;
+                tpend[s2] = 0u;
+                if (li >= NL) continue;
+                const uint32_t* src;
+                int l = li;
+                if (l < LK) {
+                    src = reinterpret_cast<const uint32_t*>(qg + t0 * DK) + 32 * l;
+                } else if ((l -= LK) < LK) {
+                    src = reinterpret_cast<const uint32_t*>(kg + t0 * DK) + 32 * l;
+                } else if ((l -= LK) < LB) {
+                    src = BS ? reinterpret_cast<const uint32_t*>(bg + t0)
+                             : reinterpret_cast<const uint32_t*>(bg + t0 * DK) + 32 * l;
+                } else if ((l -= LB) < LA) {
+                    src = AS ? reinterpret_cast<const uint32_t*>(p.la + t0) + 32 * l
+                             : reinterpret_cast<const uint32_t*>(p.la + t0 * DK) + 32 * l;
+                } else if ((l -= LA) < LV) {
+                    src = reinterpret_cast<const uint32_t*>(vg + (t0 + l) * DV + vb * VB);
+                } else {
+                    l -= LV;
+                    src = WS ? reinterpret_cast<const uint32_t*>(wg + t0)
+                             : reinterpret_cast<const uint32_t*>(wg + (t0 + l) * DV + vb * VB);
+                }
+                tpend[s2] = *src;
+            }
+        };
+
+        // operands of rows [r0, r1) of the current chunk into buffer b
+        auto emit_rows = [&](int b, int r0, int r1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                if (r < r0 || r >= r1) continue;
+                const int row = rg * RPT + r;
+                const floatx4 d = excl + gl[r] - gC;    // g_r - g_C, log2 units
+                const floatx4 eg = exp2v(d);
+                const floatx4 ek = exp2v(-d);
+                const floatx4 q4 = bf4(rq[r]);
+                const floatx4 k4 = bf4(rk[r]);
+                const floatx4 b4 = BS ? splat4(__uint_as_float(rb[r].x << 16)) : bf4(rb[r]);
+                const int so = swz<DK>(row, ch0);
+                *reinterpret_cast<half4*>(sE + b * C * DK + so) = to_h4(b4 * k4 * eg);
+                *reinterpret_cast<half4*>(sQ + b * C * DK + so) = to_h4(q4 * eg);
+                const half4 khh = to_h4(k4 * ek);
+                *reinterpret_cast<half4*>(sKr + b * C * DK + so) = khh;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) khp[j][r] = khh[j];
+            }
+        };
+
+        if (NC > 0) {
+            ld_la(0);
+            ld_qkb(0, 0, RPT);
+            ld_vw(0);
+            if (NC > 1) touch_chunk(1);
+        }
+        for (int it = 0; it <= NC; ++it) {
+            const int b = it & 1;
+            set_lane();
+            // ------------------------------------------------ segment 1
+            if (it > 0) {   // Kh^T of chunk it-1; its previous readers finished last iteration
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<KhVec*>(sKT + (ch0 + j) * LDC + rg * RPT) = khp[j];
+            }
+            if (it < NC) {
+                const int cn = it + 1 < NC ? it + 1 : it;
+                floatx4 run = zero4();
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    run += (AS ? splat4(rla[r][0]) : rla[r]) * kLog2e;
+                    gl[r] = run;
+                }
+                floatx4 incl = run;
+#pragma unroll
+                for (int d = 1; d < RGW; d *= 2) {
+                    const floatx4 t = shfl_up4(incl, d * QPW);
+                    if (rg >= d) incl += t;
+                }
+                excl = incl - run;
+                gC = shfl4(incl, (RGW - 1) * QPW + cql);
+                int over = 0;
+                if (rg == 0) {
+                    const floatx4 span = gl[0] - gC;
+                    constexpr float lim = kDecayLimit * kLog2e;
+                    over = !(span[0] <= lim && span[1] <= lim && span[2] <= lim && span[3] <= lim);
+                    *reinterpret_cast<floatx4*>(sGam + b * DK + ch0) = exp2v(gC);
+                }
+                const int anyover = __any(over);
+                if (lane == 0) sFlag[b * NPW + pw] = anyover;
+                __builtin_amdgcn_sched_barrier(0);
+                ld_la(cn);                          // decay of the next chunk: rla is free now
+                __builtin_amdgcn_sched_barrier(0);
+                emit_rows(b, 0, RH);
+                __builtin_amdgcn_sched_barrier(0);
+                ld_qkb(cn, 0, RH);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            // ------------------------------------------------ segment 2
+            if (it < NC) {
+                const int cn = it + 1 < NC ? it + 1 : it;
+                emit_rows(b, RH, RPT);
+                __builtin_amdgcn_sched_barrier(0);
+                ld_qkb(cn, RH, RPT);
+                __builtin_amdgcn_sched_barrier(0);
+                // X^T (f16) of this chunk
+#pragma unroll
+                for (int r = 0; r < XTT; ++r) {
+                    const floatx4 w4 = WS ? splat4(__uint_as_float(rw[r].x << 16)) : bf4(rw[r]);
+                    const floatx4 x = w4 * bf4(rv[r]);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        sXT[(b * VB + 4 * xcq + jj) * LDC + xtg * XTT + r] = (_Float16)x[jj];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                ld_vw(cn);
+                if (it + 2 < NC) touch_chunk(it + 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+        }
+        // never true (flag bit 31 is rejected by the API); keeps the touch loads
+        touch ^= tpend[0] ^ tpend[1];
+        if ((p.flags & 0x80000000u) && touch == 0x12345u) p.Sf[0] = 0.f;
+    } else {
+        // ======================================================== consumer
+        const int cw = wave;
+        const int col = vb * VB + 16 * cw + n_l;
+        floatx4 S[NKT];
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[mt][i] = p.S0 ? p.S0[((size_t)bh * DK + 16 * mt + m_l + i) * DV + col] : 0.f;
+        bool poisoned = false;
+
+        for (int it = 0; it <= NC; ++it) {
+            const int j = it - 1, b = j & 1;
+            // lane-derived values are recomputed from an opaque copy of the lane id each
+            // iteration, so the compiler does not keep hoisted invariants live across
+            // the loop (which would spill)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int n_l = ln & 15, g_l = ln >> 4, m_l = 4 * g_l;
+            const int col = vb * VB + 16 * cw + n_l;
+            half8 sf[NKS];
+            // ------------------------------------------------ segment 1
+            if (it > 0) {
+                int fl = 0;
+#pragma unroll
+                for (int f = 0; f < NPW; ++f) fl |= sFlag[b * NPW + f];
+                if (fl) poisoned = true;
+                if (p.states) {
+#pragma unroll
+                    for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            p.states[(((size_t)bh * NC + j) * DK + 16 * mt + m_l + i) * DV + col] = S[mt][i];
+                }
+
+                // A and P tiles: wave cw owns the diagonal A tile cw plus four of the
+                // other 16 lower tiles (6 off-diagonal A, 10 P).  The fragments of
+                // tile s+1 are loaded before the MFMAs of tile s.
+                const _Float16* eb = sE + b * C * DK;
+                const _Float16* qb = sQ + b * C * DK;
+                const _Float16* kb = sKr + b * C * DK;
+                int tP[5], tm[5], tn[5];
+                int cwo = cw;                               // scalar, recomputed per iteration
+                asm volatile("" : "+s"(cwo));
+#pragma unroll
+                for (int s = 0; s < 5; ++s) {
+                    if (s == 0) {
+                        tP[s] = 0; tm[s] = cwo; tn[s] = cwo;
+                    } else {
+                        int t = (s - 1) * NCW + cwo;        // 0..15 over the non-diagonal-A tiles
+                        if (t < 6) {                        // off-diagonal A: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                            tP[s] = 0;
+                            tm[s] = t < 1 ? 1 : (t < 3 ? 2 : 3);
+                            tn[s] = t - (tm[s] == 1 ? 0 : (tm[s] == 2 ? 1 : 3));
+                        } else {
+                            tP[s] = 1;
+                            t -= 6;
+                            int m = 0;
+                            while (t > m) { t -= m + 1; ++m; }
+                            tm[s] = m;
+                            tn[s] = t;
+                        }
+                    }
+                }
+                half8 fa[2][NKS], fb[2][NKS];
+                auto load_tile = [&](int s, int slot) {
+                    const _Float16* src = tP[s] ? qb : eb;
+#pragma unroll
+                    for (int kk = 0; kk < NKS; ++kk) {
+                        fa[slot][kk] = *reinterpret_cast<const half8*>(src + swz<DK>(16 * tm[s] + n_l, 32 * kk + 8 * g_l));
+                        fb[slot][kk] = *reinterpret_cast<const half8*>(kb + swz<DK>(16 * tn[s] + n_l, 32 * kk + 8 * g_l));
+                    }
+                };
+                load_tile(0, 0);
+#pragma unroll
+                for (int s = 0; s < 5; ++s) {
+                    if (s + 1 < 5) load_tile(s + 1, (s + 1) & 1);
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < NKS; ++kk) acc = mfma32(fa[s & 1][kk], fb[s & 1][kk], acc);
+                    const int mt = tm[s], nt = tn[s];
+                    if (tP[s]) {
+                        _Float16* dst = sP + blkP(mt, nt) * 16 * LDB;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dst[(m_l + i) * LDB + n_l] = (_Float16)((nt < mt || n_l <= m_l + i) ? acc[i] : 0.f);
+                    } else if (nt < mt) {
+                        _Float16* dst = sAn + blkA(mt, nt) * 16 * LDB;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[(m_l + i) * LDB + n_l] = (_Float16)(-acc[i]);
+                    } else {
+                        // diagonal block, transposed: sAd[blk][col][row] = A[row][col] (strict lower)
+                        floatx4 a;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) a[i] = (n_l < m_l + i) ? acc[i] : 0.f;
+                        *reinterpret_cast<floatx4*>(sAd + (mt * 16 + n_l) * LDD + m_l) = a;
+                    }
+                }
+                // inverse of the diagonal block cw of (I + A): right-looking forward
+                // substitution in fp32, column jc per lane.  The block (written by this
+                // wave above) is first read into registers, column by column.
+                {
+                    const float* ad = sAd + cw * 16 * LDD;
+                    floatx4 acol[2][4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acol[0][q] = *reinterpret_cast<const floatx4*>(ad + 4 * q);
+                    const int jc = ln & 15;
+                    float x[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < 15; ++m) {
+                        if (m + 1 < 15) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                acol[(m + 1) & 1][q] = *reinterpret_cast<const floatx4*>(ad + (m + 1) * LDD + 4 * q);
+                        }
+                        const float xm = x[m];
+#pragma unroll
+                        for (int r = m + 1; r < 16; ++r) x[r] -= acol[m & 1][r >> 2][r & 3] * xm;
+                    }
+                    if (ln < 16) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sTd[(cw * 16 + r) * LDB + jc] = (_Float16)x[r];
+                    }
+                }
+            }
+            __syncthreads();
+            // ------------------------------------------------ segment 2
+            if (it > 0) {
+                // S' = diag(gamma_C) S and its f16 fragments over channels
+#pragma unroll
+                for (int mt = 0; mt < NKT; ++mt) {
+                    const floatx4 gm = *reinterpret_cast<const floatx4*>(sGam + b * DK + 16 * mt + m_l);
+                    S[mt] = S[mt] * gm;
+                }
+#pragma unroll
+                for (int kk = 0; kk < NKS; ++kk) sf[kk] = cat8(to_h4(S[2 * kk]), to_h4(S[2 * kk + 1]));
+                // Y = [E; Qs] S'  (K = channels; lane group g holds channels 32kk+4g.. and 32kk+16+4g..)
+                floatx4 YE[4], YQ[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YE[rt] = YQ[rt] = zero4();
+                const _Float16* eb = sE + b * C * DK;
+                const _Float16* qb = sQ + b * C * DK;
+#pragma unroll
+                for (int kk = 0; kk < NKS; ++kk) {
+                    half8 ea[4], qa[4];
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const int row = 16 * rt + n_l;
+                        const int o0 = swz<DK>(row, 32 * kk + m_l), o1 = swz<DK>(row, 32 * kk + 16 + m_l);
+                        ea[rt] = cat8(ld_h4(eb + o0), ld_h4(eb + o1));
+                        qa[rt] = cat8(ld_h4(qb + o0), ld_h4(qb + o1));
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        YE[rt] = mfma32(ea[rt], sf[kk], YE[rt]);
+                        YQ[rt] = mfma32(qa[rt], sf[kk], YQ[rt]);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < NKS; ++kk) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                }
+                // small operands of the in-chunk solve, read once
+                half4 fT[4], fA[6], fP[10];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) fT[k] = ld_h4(sTd + (k * 16 + n_l) * LDB + m_l);
+#pragma unroll
+                for (int k = 0; k < 6; ++k) fA[k] = ld_h4(sAn + (k * 16 + n_l) * LDB + m_l);
+#pragma unroll
+                for (int k = 0; k < 10; ++k) fP[k] = ld_h4(sP + (k * 16 + n_l) * LDB + m_l);
+                // z_k = X_k - (E S')_k
+                floatx4 z[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    z[rt] = from_h4(ld_h4(sXT + (b * VB + 16 * cw + n_l) * LDC + 16 * rt + m_l)) - YE[rt];
+                // Block forward substitution U_k = T_kk (z_k - sum_{j<k} A_kj U_j) (A blocks
+                // stored negated).  As soon as U_k exists, its contributions to the later
+                // z, to O = Qs S' + P U and to S = S' + Kh^T U are issued, filling the
+                // latency of the substitution chain.
+                floatx4 O[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) O[rt] = YQ[rt];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    half4 kt[NKT];
+#pragma unroll
+                    for (int mt = 0; mt < NKT; ++mt) kt[mt] = ld_h4(sKT + (16 * mt + n_l) * LDC + 16 * k + m_l);
+                    const half4 uk = to_h4(mfma16(fT[k], to_h4(z[k]), zero4()));
+#pragma unroll
+                    for (int kn = k + 1; kn < 4; ++kn) z[kn] = mfma16(fA[blkA(kn, k)], uk, z[kn]);
+#pragma unroll
+                    for (int rt = k; rt < 4; ++rt) O[rt] = mfma16(fP[blkP(rt, k)], uk, O[rt]);
+#pragma unroll
+                    for (int mt = 0; mt < NKT; ++mt) S[mt] = mfma16(kt[mt], uk, S[mt]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    floatx4 o = O[rt];
+                    if (poisoned) o = splat4(__builtin_nanf(""));
+                    if (p.o) {
+                        const size_t base = (tok0 + (size_t)j * C + 16 * rt + m_l) * DV + col;
+                        if (p.flags & GDR_OUT_BF16) {
+                            uint16_t* op = reinterpret_cast<uint16_t*>(p.o);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = f32_to_bf16(o[i]);
+                        } else {
+                            float* op = reinterpret_cast<float*>(p.o);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = o[i];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (p.Sf) {
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.Sf[((size_t)bh * DK + 16 * mt + m_l + i) * DV + col] =
+                        poisoned ? __builtin_nanf("") : S[mt][i];
+        }
+    }
+}
+
+template <int DK, int DV, bool AS, bool BS, bool WS>
+static hipError_t launch_t(const FwdParams& p, hipStream_t st) {
+    using L = Layout<DK>;
+    auto kern = fwd_pipe_kernel<DK, DV, AS, BS, WS>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    dim3 grid((unsigned)(p.BH * (DV / VB))), block(64 * (NCW + NPW));
+    hipLaunchKernelGGL(kern, grid, block, L::bytes, st, p);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_modes(const FwdParams& p, hipStream_t st) {
+    const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, ws = p.flags & GDR_W_SCALAR;
+    const int m = (as ? 4 : 0) | (bs ? 2 : 0) | (ws ? 1 : 0);
+    switch (m) {
+        case 0: return launch_t<DK, DV, false, false, false>(p, st);
+        case 1: return launch_t<DK, DV, false, false, true>(p, st);
+        case 2: return launch_t<DK, DV, false, true, false>(p, st);
+        case 3: return launch_t<DK, DV, false, true, true>(p, st);
+        case 4: return launch_t<DK, DV, true, false, false>(p, st);
+        case 5: return launch_t<DK, DV, true, false, true>(p, st);
+        case 6: return launch_t<DK, DV, true, true, false>(p, st);
+        default: return launch_t<DK, DV, true, true, true>(p, st);
+    }
+}
+
+}  // namespace pipe
+
+bool fwd_pipe_supported(int dk, int dv, int chunk, uint32_t flags) {
+    if (flags & GDR_ACT_F32) return false;
+    if (chunk != 64) return false;
+    return (dk == 128 || dk == 64) && (dv == 128 || dv == 64);
+}
+
+hipError_t launch_fwd_pipe(const FwdParams& p, int dk, int dv, hipStream_t st) {
+    if (dk == 128 && dv == 128) return pipe::launch_modes<128, 128>(p, st);
+    if (dk == 64 && dv == 64) return pipe::launch_modes<64, 64>(p, st);
+    if (dk == 128 && dv == 64) return pipe::launch_modes<128, 64>(p, st);
+    if (dk == 64 && dv == 128) return pipe::launch_modes<64, 128>(p, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

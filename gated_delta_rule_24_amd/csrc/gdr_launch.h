@@ -47,6 +47,10 @@ hipError_t launch_fwd(const FwdParams& p, int dk, int dv, int chunk, hipStream_t
                       int* chunk_used);
 bool fwd_supported(int dk, int dv, int chunk, uint32_t flags);
 
+// Pipelined fast path (bf16 activations, chunk 64, d_k and d_v in {64, 128}).
+bool fwd_pipe_supported(int dk, int dv, int chunk, uint32_t flags);
+hipError_t launch_fwd_pipe(const FwdParams& p, int dk, int dv, hipStream_t st);
+
 struct BwdParams {
     const void* q;
     const void* k;

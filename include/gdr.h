@@ -69,6 +69,9 @@ typedef enum gdr_status {
 #define GDR_ALPHA_SCALAR  0x4u   /* log_alpha is one fp32 per token                   */
 #define GDR_B_SCALAR      0x8u   /* b is one value per token                          */
 #define GDR_W_SCALAR      0x10u  /* w is one value per token                          */
+#define GDR_FWD_GENERIC   0x20u  /* forward: use the single-role kernel even where the
+                                    pipelined one applies (same results up to rounding
+                                    order; for testing)                               */
 
 #define GDR_ABI_VERSION 1
 

@@ -13,14 +13,14 @@ from tests.helpers import flat_heads, oracle_fwd, rel_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, chunk=None, S0=None, out_dtype=None, return_state=True):
+def _run(inp, chunk=None, S0=None, out_dtype=None, return_state=True, generic=False):
     import torch
     import gated_delta_rule_24_amd as gdr
     d = to_dev(inp)
     s0 = d["S0"] if S0 is None else S0
     o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], s0,
                           chunk=chunk or inp.chunk, out_dtype=out_dtype or torch.float32,
-                          return_state=return_state)
+                          return_state=return_state, generic=generic)
     torch.cuda.synchronize()
     return o, sf
 
@@ -63,6 +63,15 @@ SMALL = [
     ("dk64_dv128", dict(B=1, H=2, T=192, dk=64, dv=128), 2e-2),
     ("dk128_dv64", dict(B=1, H=2, T=192, dk=128, dv=64), 2e-2),
     ("erase_range_0_2", dict(B=1, H=2, T=256, dk=128, dv=128, gate_hi=2.0), 2e-2),
+    ("alpha_scalar_only", dict(B=1, H=2, T=128, dk=128, dv=128, alpha_mode="scalar"), 2e-2),
+    ("alpha_scalar_b_scalar", dict(B=1, H=2, T=128, dk=128, dv=128, alpha_mode="scalar",
+                                   b_mode="scalar"), 2e-2),
+    ("alpha_scalar_w_scalar", dict(B=1, H=2, T=128, dk=128, dv=128, alpha_mode="scalar",
+                                   w_mode="scalar"), 2e-2),
+    ("b_w_scalar_untied", dict(B=1, H=2, T=128, dk=128, dv=128, b_mode="scalar",
+                               w_mode="scalar"), 2e-2),
+    ("single_chunk", dict(B=3, H=1, T=64, dk=128, dv=128), 2e-2),
+    ("two_chunks", dict(B=1, H=1, T=128, dk=128, dv=128), 2e-2),
     ("f32_d128_c64", dict(B=1, H=2, T=256, dk=128, dv=128, act="f32"), 1e-4),
     ("f32_d128_c32", dict(B=1, H=2, T=160, dk=128, dv=128, act="f32", chunk=32), 1e-4),
     ("f32_d64_c64", dict(B=1, H=2, T=192, dk=64, dv=64, act="f32"), 1e-4),
@@ -81,6 +90,26 @@ def test_small_cases(name, kw, tol):
     inp = _case(name, **kw)
     o, sf = _run(inp)
     _check(inp, o, sf, tol)
+
+
+GENERIC = [
+    ("gdn2_generic", dict(B=2, H=2, T=256, dk=128, dv=128)),
+    ("gdn_generic", dict(B=1, H=2, T=192, dk=128, dv=128, alpha_mode="scalar", b_mode="scalar",
+                         w_mode="scalar", tied=True, s0_std=None)),
+    ("d64_generic", dict(B=1, H=3, T=128, dk=64, dv=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", GENERIC, ids=[c[0] for c in GENERIC])
+def test_generic_kernel_matches_oracle_and_pipelined(name, kw):
+    """The single-role kernel (selected by GDR_FWD_GENERIC) on shapes the
+    pipelined kernel also serves: both meet the tolerance, and they agree."""
+    inp = _case(name, **kw)
+    og, sg = _run(inp, generic=True)
+    _check(inp, og, sg, 2e-2)
+    op, sp = _run(inp)
+    assert rel_err(og.cpu().numpy(), op.cpu().numpy()) <= 1e-2
+    assert rel_err(sg.cpu().numpy(), sp.cpu().numpy()) <= 1e-2
 
 
 def test_zero_initial_state_pointer_equals_zeros():
