@@ -88,6 +88,23 @@ def test_decode_argument_validation():
 
 def test_bwd_workspace_query_and_validation():
     lib = _lib()
-    n = lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0)
-    assert n == 0 or n >= 2 * 2 * 2 * 128 * 128 * 4
+    # chunk-start states and chunk-end gradients: 2 x B*H x T/chunk x d_k x d_v fp32
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0) == 2 * 2 * 2 * 128 * 128 * 4
+    # fp32 activations block the backward with chunks of 32
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 64, 1) == 2 * 2 * 4 * 64 * 64 * 4
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 48, 0) == 0
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 32, 32, 64, 0) == 0
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 64, 64, 0) == 0
+
+    def call(ws=A, nbytes=1 << 30, **kw):
+        a = dict(B=1, H=2, T=128, dk=128, dv=128, chunk=64, flags=0)
+        a.update(kw)
+        return lib.gdr_chunk_bwd(A, A, A, A, A, A, A, A, None, A, A, A, A, A, A, A, a["B"], a["H"],
+                                 a["T"], a["dk"], a["dv"], a["chunk"], a["flags"], ws, nbytes, None)
+    assert call(ws=None) == 3
+    assert call(nbytes=1000) == 3
+    assert call(T=100) == 1
+    assert call(flags=0x2) == 1          # bf16 output has no meaning for gradients
+    assert call(ws=MIS) == 1
+    assert call(dk=32, dv=32) == 2
+    assert call(chunk=16) == 2

@@ -1,0 +1,160 @@
+"""GPU parity of gdr_chunk_bwd against the oracle's fp64 reverse mode.
+
+Loss L = <dO, o> + <dS_final, S_final>.  Tolerances per gradient tensor
+(max|Δ|/rms(ref) over the whole tensor): 1e-4 with fp32 activations, 2e-2
+with bf16 activations, the forward's thresholds.  For a scalar gate the
+oracle's per-channel gradient is summed over the broadcast axis; tied gates
+(one buffer passed as b and w) get db and dw separately, whose sum is the
+buffer's gradient."""
+import numpy as np
+import pytest
+
+import gdr_synth as gs
+import oracle
+from tests.helpers import rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
+
+
+def _case(name, **kw):
+    print(f"bwd case {name} {kw}", flush=True)
+    return gs.preset(name, **kw) if name in gs.PRESETS else gs.make_inputs(with_dO=True, **kw)
+
+
+def _dsf(inp, seed=7):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((inp.B, inp.H, inp.dk, inp.dv)) * 0.5).astype(np.float32)
+
+
+def _run(inp, dSf=None, chunk=None):
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    d = to_dev(inp)
+    s0 = d["S0"]
+    if s0 is None:
+        s0 = torch.zeros((inp.B, inp.H, inp.dk, inp.dv), dtype=torch.float32, device="cuda")
+    dsf = None if dSf is None else torch.from_numpy(dSf).cuda()
+    g = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], s0, d["dO"], dsf,
+                      chunk=chunk or inp.chunk)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in g.items()}
+
+
+def _ref(inp, dSf=None, heads=None):
+    a = inp.arrays
+    B, H = inp.B, inp.H
+
+    def sel(x):
+        if x is None:
+            return None
+        x = x.reshape((B * H,) + x.shape[2:])
+        return x if heads is None else x[np.asarray(heads)]
+    s0 = sel(a["S0"]) if a["S0"] is not None else None
+    ref = oracle.bwd(sel(a["q"]), sel(a["k"]), sel(a["v"]), sel(a["log_alpha"]), sel(a["b"]),
+                     sel(a["w"]), s0, sel(a["dO"]), None if dSf is None else sel(dSf))
+    if inp.alpha_mode == "scalar":
+        ref["dlog_alpha"] = ref["dlog_alpha"].sum(-1)
+    if inp.b_mode == "scalar":
+        ref["db"] = ref["db"].sum(-1)
+    if inp.w_mode == "scalar":
+        ref["dw"] = ref["dw"].sum(-1)
+    return ref
+
+
+def _check(inp, got, ref, tol, heads=None):
+    errs = {}
+    for n in GRADS:
+        g = got[n].reshape((inp.B * inp.H,) + got[n].shape[2:])
+        if heads is not None:
+            g = g[np.asarray(heads)]
+        errs[n] = rel_err(g, ref[n])
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol})", flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, bad
+    return errs
+
+
+CASES = [
+    # name, kwargs, tol, with dS_final
+    ("gdn2_bf16_d128_c64", dict(B=1, H=2, T=256, dk=128, dv=128), 2e-2, False),
+    ("gdn2_bf16_d128_c64_dsf", dict(B=2, H=1, T=192, dk=128, dv=128), 2e-2, True),
+    ("gdn2_bf16_d128_c32", dict(B=1, H=2, T=160, dk=128, dv=128, chunk=32), 2e-2, True),
+    ("gdn2_bf16_d64_c64", dict(B=2, H=2, T=256, dk=64, dv=64), 2e-2, True),
+    ("gdn2_bf16_d64_c32", dict(B=1, H=3, T=96, dk=64, dv=64, chunk=32), 2e-2, False),
+    ("gdn_scalar_tied", dict(B=1, H=2, T=192, dk=128, dv=128, alpha_mode="scalar",
+                             b_mode="scalar", w_mode="scalar", tied=True, s0_std=None), 2e-2, False),
+    ("kda_tied", dict(B=1, H=2, T=192, dk=64, dv=64, b_mode="scalar", w_mode="scalar",
+                      tied=True), 2e-2, True),
+    ("b_only_channel", dict(B=1, H=2, T=128, dk=64, dv=64, w_mode="scalar"), 2e-2, False),
+    ("w_only_channel", dict(B=1, H=2, T=128, dk=64, dv=64, b_mode="scalar"), 2e-2, False),
+    ("alpha_scalar_channel_bw", dict(B=1, H=2, T=128, dk=128, dv=128, alpha_mode="scalar"),
+     2e-2, True),
+    ("erase_range_0_2", dict(B=1, H=2, T=192, dk=128, dv=128, gate_hi=2.0), 2e-2, False),
+    ("single_chunk", dict(B=2, H=1, T=64, dk=128, dv=128), 2e-2, True),
+    ("f32_d128", dict(B=1, H=2, T=128, dk=128, dv=128, act="f32"), 1e-4, True),
+    ("f32_d64_c32", dict(B=1, H=2, T=96, dk=64, dv=64, act="f32", chunk=32), 1e-4, False),
+    ("f32_scalar_gdn", dict(B=1, H=2, T=96, dk=64, dv=64, act="f32", chunk=32, alpha_mode="scalar",
+                            b_mode="scalar", w_mode="scalar", tied=True), 1e-4, True),
+    ("f32_strong_decay", dict(B=1, H=1, T=128, dk=64, dv=64, act="f32", decay_scale=0.5), 1e-4, True),
+]
+
+
+@pytest.mark.parametrize("name,kw,tol,dsf", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_reverse_mode(name, kw, tol, dsf):
+    inp = _case(name, **kw)
+    dSf = _dsf(inp) if dsf else None
+    got = _run(inp, dSf)
+    _check(inp, got, _ref(inp, dSf), tol)
+
+
+def test_backward_deterministic_bitwise():
+    inp = _case("det", B=1, H=2, T=192, dk=128, dv=128)
+    g1 = _run(inp)
+    g2 = _run(inp)
+    for n in GRADS:
+        assert np.array_equal(g1[n], g2[n]), n
+
+
+def test_backward_chunk_invariance():
+    """Chunks of 32 and 64 are two blockings of the same gradients."""
+    inp = _case("chunks", B=1, H=2, T=192, dk=128, dv=128)
+    ref = _ref(inp)
+    e64 = _check(inp, _run(inp, chunk=64), ref, 2e-2)
+    e32 = _check(inp, _run(inp, chunk=32), ref, 2e-2)
+    assert max(e64.values()) < 2e-2 and max(e32.values()) < 2e-2
+
+
+def test_backward_empty_sequence_passes_state_gradient():
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    B, H, dk = 2, 3, 64
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")
+    q = z(B, H, 0, dk)
+    la = z(B, H, 0, dk, dt=torch.float32)
+    dsf = torch.randn(B, H, dk, dk, device="cuda")
+    g = gdr.chunk_bwd(q, q, q, la, q, q, z(B, H, dk, dk, dt=torch.float32), q, dsf, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"], dsf)
+    g = gdr.chunk_bwd(q, q, q, la, q, q, z(B, H, dk, dk, dt=torch.float32), q, None, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g["dS0"]).item() == 0
+
+
+def test_backward_decay_beyond_f16_range_is_loud():
+    """A chunk whose in-chunk decay exceeds the f16 operand range yields NaN
+    gradients (never silently wrong values)."""
+    inp = _case("strong", B=1, H=1, T=128, dk=64, dv=64, decay_scale=1.0)
+    g = _run(inp)
+    assert np.isnan(g["dq"]).any() and np.isnan(g["dS0"]).any()
+
+
+def test_gdn2_backward_full_workload_sampled_heads():
+    """The 32-head x 16384-token backward workload, checked on sampled heads."""
+    inp = _case("gdn2_bwd")
+    got = _run(inp)
+    heads = [0, 17]
+    _check(inp, got, _ref(inp, heads=heads), 2e-2, heads=heads)
+    for n in GRADS:
+        assert np.isfinite(got[n]).all(), n
