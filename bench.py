@@ -51,6 +51,13 @@ DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + 
 
 # the timed launch runs the pipelined kernel; the counters in the traffic summary
 # are only used while these sources are unchanged
+# backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
+# head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
+# d log-decay, db, dv, dw fp32; plus S0 read and dS0 written per head
+BB, BH_, BT = 1, 32, 16384
+BWD_BYTES_PER_TOKEN = 6 * FD * 2 + FD * 4 + 6 * FD * 4
+BWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
+
 FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_pipe.hip",
                       "gated_delta_rule_24_amd/csrc/gdr_device.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
@@ -124,10 +131,12 @@ def bench_fwd(steps, warmup):
     o = torch.empty((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
     Sf = torch.empty((FB, FH, FD, FD), dtype=torch.float32, device="cuda")
     flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    nbytes = gdr.gdr_chunk_fwd_workspace_bytes(FB, FH, FT, FD, FD, FC, flags)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
 
     def step():
         gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], o, Sf,
-                          FB, FH, FT, FD, FD, FC, flags)
+                          FB, FH, FT, FD, FD, FC, flags, ws, nbytes)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
     return inp, wall_ms, ev_ms
 
@@ -163,6 +172,29 @@ def bench_copy(steps, warmup):
     return wall_ms, ev_ms
 
 
+def bench_bwd(steps, warmup):
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    inp = gs.preset("gdn2_bwd", seed=0)
+    d = upload(inp)
+    f32 = torch.float32
+    shp_k, shp_v = (BB, BH_, BT, FD), (BB, BH_, BT, FD)
+    g = {n: torch.empty(shp_k, dtype=f32, device="cuda") for n in ("dq", "dk", "dla", "db")}
+    g.update({n: torch.empty(shp_v, dtype=f32, device="cuda") for n in ("dv", "dw")})
+    dS0 = torch.empty((BB, BH_, FD, FD), dtype=f32, device="cuda")
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    nbytes = gdr.gdr_chunk_bwd_workspace_bytes(BB, BH_, BT, FD, FD, FC, flags)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"],
+                          None, g["dq"], g["dk"], g["dv"], g["dla"], g["db"], g["dw"], dS0,
+                          BB, BH_, BT, FD, FD, FC, flags, ws, nbytes)
+    wall_ms, ev_ms = time_loop(step, steps, warmup)
+    return wall_ms, ev_ms, nbytes
+
+
 def cpu_baseline(inp, min_seconds=10.0, max_passes=50):
     """The fp64 oracle on this host over the same GDN-2 workload, repeated
     until about `min_seconds` of CPU work have been timed."""
@@ -189,7 +221,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy"], default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -213,6 +245,11 @@ def main():
         w, e = bench_decode(args.steps, args.warmup)
         log(f"decode: {e * 1e3:.1f} us/step, {DN * DH * DEC_BYTES_PER_HEAD / e / 1e6:.1f} GB/s")
         return
+    bwd_bytes = BB * BH_ * BT * BWD_BYTES_PER_TOKEN + BB * BH_ * BWD_STATE_BYTES_PER_HEAD
+    if args.only == "bwd":
+        w, e, _ = bench_bwd(args.steps, args.warmup)
+        log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
+        return
 
     inp, wall_ms, ev_ms = bench_fwd(args.steps, args.warmup)
     ntok = FB * FH * FT
@@ -227,6 +264,10 @@ def main():
     dec_wall, dec_ev = bench_decode(max(args.steps, 10), args.warmup)
     dec_gbs = DN * DH * DEC_BYTES_PER_HEAD / (dec_ev * 1e-3) / 1e9
     log(f"decode: {dec_ev * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+
+    bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
+    bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
+    log(f"bwd: {bwd_ev * 1e3:.1f} us/step, {bwd_gbs:.0f} GB/s")
 
     traffic = measured_traffic()
     result = {
@@ -273,6 +314,15 @@ def main():
             "GB_per_s": dec_gbs,
             "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
             "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
+        },
+        "backward": {
+            "workload": "gdn2_chunk_bwd B=1 H=32 T=16384 d_k=d_v=128 chunk=64, dO only",
+            "us_per_step": bwd_ev * 1e3,
+            "head_tokens_per_s": BB * BH_ * BT / (bwd_ev * 1e-3),
+            "GB_per_s": bwd_gbs,
+            "frac_hbm_peak": bwd_gbs / HBM_PEAK_GBS,
+            "bytes_per_step": bwd_bytes,
+            "workspace_bytes": bwd_ws,
         },
     }
     if not args.no_cpu_baseline:

@@ -58,7 +58,9 @@ def _load():
         lib.gdr_abi_version.restype = I
         lib.gdr_status_string.argtypes = [I]
         lib.gdr_status_string.restype = ctypes.c_char_p
-        lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 6 + [U, P]
+        lib.gdr_chunk_fwd_workspace_bytes.argtypes = [I] * 6 + [U]
+        lib.gdr_chunk_fwd_workspace_bytes.restype = S
+        lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 6 + [U, P, S, P]
         lib.gdr_chunk_fwd.restype = I
         lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 4 + [U, P]
         lib.gdr_decode_step.restype = I
@@ -75,7 +77,8 @@ def lib():
     return _load()
 
 
-EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd",
+EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
+                    "gdr_chunk_fwd",
                     "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd")
 
 
@@ -124,11 +127,15 @@ def _check(fn, st):
 # ---------------------------------------------------------------------------
 
 
+def gdr_chunk_fwd_workspace_bytes(B, H, T, d_k, d_v, chunk, flags) -> int:
+    return int(_load().gdr_chunk_fwd_workspace_bytes(B, H, T, d_k, d_v, chunk, flags))
+
+
 def gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, B, H, T, d_k, d_v, chunk,
-                  flags, stream=None):
+                  flags, workspace=None, workspace_bytes=0, stream=None):
     st = _load().gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, d_k, d_v, chunk,
-                               flags, _stream(stream))
+                               flags, _ptr(workspace), workspace_bytes, _stream(stream))
     _check("gdr_chunk_fwd", st)
 
 
@@ -160,9 +167,11 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_a
 
 def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
               out_dtype=torch.float32, return_state: bool = True, stream=None,
-              generic: bool = False):
+              generic: bool = False, path: str = "auto"):
     """q, k: [B,H,T,dk]; v: [B,H,T,dv]; log_alpha, b: [B,H,T,dk] or [B,H,T];
     w: [B,H,T,dv] or [B,H,T]; S0: [B,H,dk,dv] fp32 or None.
+    path "auto" passes a workspace (two-pass kernels where they apply),
+    "fused" passes none (single-kernel path).
     Returns (o [B,H,T,dv], S_final [B,H,dk,dv] or None)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -173,7 +182,15 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
         flags |= GDR_FWD_GENERIC
     o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
     Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
-    gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, Sf, B, H, T, dk, dv, chunk, flags, stream)
+    ws, nbytes = None, 0
+    if path == "auto":
+        nbytes = gdr_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, flags)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif path != "fused":
+        raise ValueError(f"unknown path {path!r}")
+    gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, Sf, B, H, T, dk, dv, chunk, flags, ws, nbytes,
+                  stream)
     return o, Sf
 
 

@@ -56,21 +56,32 @@ const char* gdr_status_string(gdr_status s) {
     return "unknown status";
 }
 
+size_t gdr_chunk_fwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                     uint32_t flags) {
+    if (B < 1 || H < 1 || T < 1 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
+    if (T % chunk != 0 || (long long)B * H > (1LL << 28)) return 0;
+    if (!gdr::fwd_wy_supported(d_k, d_v, chunk, flags)) return 0;
+    return gdr::fwd_wy_workspace_bytes(B * H, T, d_k, d_v);
+}
+
 gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                          const void* b, const void* w, const float* S0, void* o, float* S_final,
                          int B, int H, int T, int d_k, int d_v, int chunk, uint32_t flags,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
     if (flags & ~kKnownFlags) return GDR_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
     if (!(chunk == 16 || chunk == 32 || chunk == 64)) return GDR_ERR_INVALID_ARG;
     if (T % chunk != 0) return GDR_ERR_INVALID_ARG;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final};
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
     if ((long long)B * H > (1LL << 28) || (long long)B * H * T > (1LL << 40)) return GDR_ERR_INVALID_ARG;
     if (!gdr::fwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
+    const size_t need = gdr_chunk_fwd_workspace_bytes(B, H, T, d_k, d_v, chunk, flags);
+    const bool two_pass = workspace != nullptr && need > 0;
+    if (two_pass && workspace_bytes < need) return GDR_ERR_WORKSPACE;
     gdr_status ds = check_device();
     if (ds != GDR_OK) return ds;
 
@@ -78,6 +89,7 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
     p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr;
     p.BH = B * H; p.T = T; p.flags = flags;
+    if (two_pass) return from_hip(gdr::launch_fwd_wy(p, d_k, d_v, workspace, (hipStream_t)stream));
     int used = 0;
     return from_hip(gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used));
 }

@@ -169,6 +169,15 @@ template <> struct Mma<float> {
     }
 };
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations, then all waves meet.  Unlike __syncthreads() it does not drain
+// the wave's global loads and stores (vmcnt), so prefetches and output stores
+// stay in flight across it.  Global memory written before it is not made
+// visible to the other waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ floatx4 zero4() {
     floatx4 z;
     z[0] = z[1] = z[2] = z[3] = 0.f;

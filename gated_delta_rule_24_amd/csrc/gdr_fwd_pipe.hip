@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams
                 ld_qkb(cn, 0, RH);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
+            lds_barrier();
             // ------------------------------------------------ segment 2
             if (it < NC) {
                 const int cn = it + 1 < NC ? it + 1 : it;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams
                 if (it + 2 < NC) touch_chunk(it + 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
+            lds_barrier();
         }
         // never true (flag bit 31 is rejected by the API); keeps the touch loads
         touch ^= tpend[0] ^ tpend[1];
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // ------------------------------------------------ segment 2
             if (it > 0) {
                 // S' = diag(gamma_C) S and its f16 fragments over channels
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (p.Sf) {
 #pragma unroll

@@ -1,0 +1,863 @@
+// Two-pass chunkwise forward of the gated delta rule (bf16 activations, chunk
+// 64, d_k and d_v in {64, 128}); used when the caller provides a workspace.
+//
+// The WY form of a chunk (Gated DeltaNet-2 Q&A page, Q4; "Gated DeltaNet-2
+// Review" §3-2 item 5) splits into a part that does not depend on the state
+// and a short state chain.  With E, Qs, Kh, X, A, P as in the other forward
+// kernels, T = (I + A)^-1 and
+//   W = T E,   Ũ = T X,   Q̃ = Qs - P W,
+// the chunk update is
+//   S' = diag(e^{g_C}) S,   U = Ũ - W S',   O = Q̃ S' + P Ũ,   S <- S' + Kh^T U.
+//
+// Pass 1 (wy_kernel) computes W, Q̃, Ũ, P, Kh^T and e^{g_C} for every chunk of
+// every head in parallel: all the element-wise gate work, the exponentials and
+// the triangular inverse happen here, once per chunk.  It writes them to the
+// workspace as ready-made MFMA fragments (each 16-byte lane piece in the order
+// the state pass reads it).
+// Pass 2 (chain_kernel) runs the state chain: one workgroup per (head, two
+// 16-column strips of the state).  One wave keeps the fp32 strips in MFMA
+// accumulators and issues only the chain (Y = W S', U = Ũ - Y, S += Kh^T U);
+// a second wave computes the chunk's output O = Q̃ S' + P Ũ from the S'
+// fragments the first publishes in LDS.  Both read their fragments directly
+// from the workspace (L2) one chunk ahead of use, and the chunks after that
+// are touched so they are already in L2.  Every fragment feeds both strips.
+#include "gdr_device.h"
+#include "gdr_launch.h"
+
+namespace gdr {
+
+namespace wy {
+
+constexpr int C = 64;
+constexpr int NT = 256;
+constexpr float kDecayLimit = 10.0f;    // f16 operand range, as in the other kernels
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-chunk record in the workspace (bytes).  Fragment blocks are 64 lanes x
+// 16 bytes; lane l = r + 16 g (r = l & 15, g = l >> 4) holds, for a 32-wide
+// K step kk, the K positions 32kk + 4g .. +3 followed by 32kk + 16 + 4g .. +3.
+//   W, Q̃  block (rt, kk): row t = 16 rt + r of W (Q̃), K = channels
+//   Kh^T   block (mt, kk): channel 16 mt + r of Kh^T, K = tokens
+//   P      block (rt, kk): row 16 rt + r of P, K = tokens
+//   Ũ      strip nt, block kk: column 16 nt + r of Ũ, K = tokens
+//   G      e^{g_C} per channel (fp32), then an int flag (decay out of range)
+template <int DK, int DV>
+struct Rec {
+    static constexpr size_t W = 0;
+    static constexpr size_t Q = W + (size_t)C * DK * 2;
+    static constexpr size_t K = Q + (size_t)C * DK * 2;
+    static constexpr size_t P = K + (size_t)DK * C * 2;
+    static constexpr size_t U = P + (size_t)C * C * 2;
+    static constexpr size_t G = U + (size_t)C * DV * 2;
+    static constexpr size_t bytes = G + (((size_t)DK * 4 + 16 + 255) & ~size_t(255));
+    static constexpr size_t strip = (size_t)C * 16 * 2;   // Ũ bytes per 16-column strip
+};
+
+__device__ __forceinline__ half4 to_h4(floatx4 v) {
+    half4 h;
+    h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
+    return h;
+}
+__device__ __forceinline__ half8 cat8(half4 a, half4 b) {
+    half8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+__device__ __forceinline__ half4 lo4(half8 v) {
+    half4 r;
+    r[0] = v[0]; r[1] = v[1]; r[2] = v[2]; r[3] = v[3];
+    return r;
+}
+__device__ __forceinline__ half4 hi4(half8 v) {
+    half4 r;
+    r[0] = v[4]; r[1] = v[5]; r[2] = v[6]; r[3] = v[7];
+    return r;
+}
+__device__ __forceinline__ floatx4 f4(half4 h) {
+    floatx4 v;
+    v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
+    return v;
+}
+__device__ __forceinline__ floatx4 mfma16(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma32(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
+__device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+// four K values of a column (stride ld)
+__device__ __forceinline__ half4 ld_col4(const _Float16* p, int ld) {
+    half4 h;
+    h[0] = p[0]; h[1] = p[ld]; h[2] = p[2 * ld]; h[3] = p[3 * ld];
+    return h;
+}
+
+// ---------------------------------------------------------------------------
+// pass 1: chunk-local WY operands
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct PrepLayout {
+    static constexpr int LDE = DK + 8;      // E, Qs, Kh rows        [C][LDE]  f16
+    static constexpr int LDT = C + 8;       // token-contiguous rows  [*][LDT]  f16
+    static constexpr int LDA = C + 4;       // A                      [C][LDA]  fp32
+    static constexpr int CO = DK / 8;       // key-side channel octets per row
+    static constexpr int NPART = NT / CO;   // token parts of the key-side mapping
+    static constexpr int TPP = C / NPART;   // tokens per thread
+    static constexpr int VO = DV / 8;
+    static constexpr int XPART = NT / VO;
+    static constexpr int XTP = C / XPART;
+    static constexpr size_t oE = 0;
+    static constexpr size_t oQ = oE + (size_t)C * LDE * 2;
+    static constexpr size_t oK = oQ + (size_t)C * LDE * 2;
+    static constexpr size_t oEt = oK + (size_t)C * LDE * 2;     // E^T  [DK][LDT]
+    static constexpr size_t oXt = oEt + (size_t)DK * LDT * 2;   // X^T  [DV][LDT]
+    static constexpr size_t oWt = oXt + (size_t)DV * LDT * 2;   // W^T  [DK][LDT]
+    static constexpr size_t oT = oWt + (size_t)DK * LDT * 2;    // T    [C][LDT]
+    static constexpr size_t oP = oT + (size_t)C * LDT * 2;      // P    [C][LDT]
+    static constexpr size_t oZ = oP + (size_t)C * LDT * 2;      // Z^T  [C/2][LDT]
+    static constexpr size_t oA = oZ + (size_t)(C / 2) * LDT * 2;
+    static constexpr size_t oTot = oA + (size_t)C * LDA * 4;    // [NPART][DK] fp32
+    static constexpr int LDD = 20;                               // diagonal blocks of A, transposed
+    static constexpr size_t oAd = oTot + (size_t)NPART * DK * 4; // [C/16][16][LDD] fp32
+    static constexpr size_t oFl = oAd + (size_t)(C / 16) * 16 * LDD * 4;   // [NT/64] int
+    static constexpr size_t bytes = oFl + (size_t)(NT / 64) * 4;
+};
+
+template <int DK, int DV, bool AS, bool BS, bool WS>
+__global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* ws) {
+    using L = PrepLayout<DK, DV>;
+    using R = Rec<DK, DV>;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    static_assert(L::NPART >= 1 && L::TPP >= 1 && L::XTP >= 1, "mapping");
+    constexpr int LDE = L::LDE, LDT = L::LDT, LDA = L::LDA;
+    constexpr int CO = L::CO, TPP = L::TPP, VO = L::VO, XTP = L::XTP;
+    constexpr int NB = C / 16, NKK = DK / 32, NST = DV / 16;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    _Float16* sE = reinterpret_cast<_Float16*>(smem + L::oE);
+    _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::oQ);
+    _Float16* sK = reinterpret_cast<_Float16*>(smem + L::oK);
+    _Float16* sEt = reinterpret_cast<_Float16*>(smem + L::oEt);
+    _Float16* sXt = reinterpret_cast<_Float16*>(smem + L::oXt);
+    _Float16* sWt = reinterpret_cast<_Float16*>(smem + L::oWt);
+    _Float16* sT = reinterpret_cast<_Float16*>(smem + L::oT);
+    _Float16* sP = reinterpret_cast<_Float16*>(smem + L::oP);
+    _Float16* sZ = reinterpret_cast<_Float16*>(smem + L::oZ);
+    float* sA = reinterpret_cast<float*>(smem + L::oA);
+    float* sTot = reinterpret_cast<float*>(smem + L::oTot);
+    float* sAd = reinterpret_cast<float*>(smem + L::oAd);
+    int* sFl = reinterpret_cast<int*>(smem + L::oFl);
+    constexpr int LDD = L::LDD;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+    const int co = tid % CO, part = tid / CO;       // channels 8co.., tokens part*TPP..
+    const int vo = tid % VO, xpart = tid / VO;      // columns 8vo.., tokens xpart*XTP..
+    const int NC = p.T / C;
+    const int total = p.BH * NC;
+    const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b);
+    const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v);
+    const uint16_t* wg = reinterpret_cast<const uint16_t*>(p.w);
+
+    // upper tiles of T and P stay zero (only lower tiles are written per chunk)
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int r = idx / C, c = idx % C;
+        if ((c >> 4) > (r >> 4)) {
+            sT[r * LDT + c] = (_Float16)0.f;
+            sP[r * LDT + c] = (_Float16)0.f;
+        }
+    }
+
+    // raw inputs of one chunk: 8 channels x TPP tokens (key side), 8 columns x XTP
+    // tokens (value side), in 16-byte loads (few enough to stay in flight together)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 rq[TPP], rk[TPP], rb[TPP], rv[XTP], rw[XTP];
+    floatx4 rla[TPP][2];
+    auto issue = [&](int idx) {
+        const int bh = idx / NC, c = idx % NC;
+        const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+#pragma unroll
+        for (int j = 0; j < TPP; ++j) {
+            const size_t t = tok0 + part * TPP + j;
+            const size_t ix = t * DK + 8 * co;
+            rq[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + ix);
+            rk[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + ix);
+            if constexpr (BS) rb[j][0] = bg[t];
+            else rb[j] = *reinterpret_cast<const u32x4*>(bg + ix);
+            if constexpr (AS) {
+                rla[j][0][0] = p.la[t];
+            } else {
+                rla[j][0] = *reinterpret_cast<const floatx4*>(p.la + ix);
+                rla[j][1] = *reinterpret_cast<const floatx4*>(p.la + ix + 4);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < XTP; ++j) {
+            const size_t t = tok0 + xpart * XTP + j;
+            const size_t ix = t * DV + 8 * vo;
+            rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
+            if constexpr (WS) rw[j][0] = wg[t];
+            else rw[j] = *reinterpret_cast<const u32x4*>(wg + ix);
+        }
+    };
+    auto unpack8 = [](u32x4 u, float (&f)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    };
+
+    int idx = blockIdx.x;
+    if (idx < total) issue(idx);
+    for (; idx < total; idx += gridDim.x) {
+        unsigned char* rec = ws + (size_t)idx * R::bytes;
+        // ---------------- element-wise: in-chunk prefix, E, Qs, Kh, X (fp32 -> f16)
+        float gl[TPP][8];
+        {
+            float run[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) run[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < TPP; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    run[i] += (AS ? rla[j][0][0] : rla[j][i >> 2][i & 3]) * kLog2e;
+                    gl[j][i] = run[i];
+                }
+            floatx4 r0, r1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { r0[i] = run[i]; r1[i] = run[4 + i]; }
+            *reinterpret_cast<floatx4*>(sTot + part * DK + 8 * co) = r0;
+            *reinterpret_cast<floatx4*>(sTot + part * DK + 8 * co + 4) = r1;
+        }
+        lds_barrier();
+        int over = 0;
+        {
+            floatx4 off[2] = {zero4(), zero4()}, gC[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int q = 0; q < L::NPART; ++q) {
+                const floatx4 t0 = *reinterpret_cast<const floatx4*>(sTot + q * DK + 8 * co);
+                const floatx4 t1 = *reinterpret_cast<const floatx4*>(sTot + q * DK + 8 * co + 4);
+                if (q < part) { off[0] += t0; off[1] += t1; }
+                gC[0] += t0;
+                gC[1] += t1;
+            }
+            if (part == 0) {
+                constexpr float lim = kDecayLimit * kLog2e;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) over |= !(gl[0][i] - gC[i >> 2][i & 3] <= lim);
+                floatx4 e0, e1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e0[i] = __builtin_amdgcn_exp2f(gC[0][i]);
+                    e1[i] = __builtin_amdgcn_exp2f(gC[1][i]);
+                }
+                *reinterpret_cast<floatx4*>(rec + R::G + 32 * co) = e0;
+                *reinterpret_cast<floatx4*>(rec + R::G + 32 * co + 16) = e1;
+            }
+            _Float16 et[8][TPP];
+#pragma unroll
+            for (int j = 0; j < TPP; ++j) {
+                const int t = part * TPP + j;
+                float q8[8], k8[8], b8[8];
+                unpack8(rq[j], q8);
+                unpack8(rk[j], k8);
+                if constexpr (BS) {
+                    const float bs = __uint_as_float(rb[j][0] << 16);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) b8[i] = bs;
+                } else {
+                    unpack8(rb[j], b8);
+                }
+                half8 e, qq, kk;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float d = off[i >> 2][i & 3] + gl[j][i] - gC[i >> 2][i & 3];
+                    const float eg = __builtin_amdgcn_exp2f(d), ek = __builtin_amdgcn_exp2f(-d);
+                    e[i] = (_Float16)(b8[i] * k8[i] * eg);
+                    qq[i] = (_Float16)(q8[i] * eg);
+                    kk[i] = (_Float16)(k8[i] * ek);
+                    et[i][j] = e[i];
+                }
+                *reinterpret_cast<half8*>(sE + t * LDE + 8 * co) = e;
+                *reinterpret_cast<half8*>(sQ + t * LDE + 8 * co) = qq;
+                *reinterpret_cast<half8*>(sK + t * LDE + 8 * co) = kk;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < TPP; j += 2) {
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    h2 v;
+                    v[0] = et[i][j];
+                    v[1] = et[i][j + 1];
+                    *reinterpret_cast<h2*>(sEt + (8 * co + i) * LDT + part * TPP + j) = v;
+                }
+            _Float16 xt[8][XTP];
+#pragma unroll
+            for (int j = 0; j < XTP; ++j) {
+                float v8[8], w8[8];
+                unpack8(rv[j], v8);
+                if constexpr (WS) {
+                    const float wsv = __uint_as_float(rw[j][0] << 16);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) w8[i] = wsv;
+                } else {
+                    unpack8(rw[j], w8);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xt[i][j] = (_Float16)(v8[i] * w8[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < XTP; j += 2) {
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    h2 v;
+                    v[0] = xt[i][j];
+                    v[1] = xt[i][j + 1];
+                    *reinterpret_cast<h2*>(sXt + (8 * vo + i) * LDT + xpart * XTP + j) = v;
+                }
+        }
+        {
+            // block-wide OR of the decay check through LDS
+            const int any = __any(over);
+            if (lane == 0) sFl[wave] = any;
+            lds_barrier();
+            over = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) over |= sFl[w];
+        }
+        if (tid == 0) *reinterpret_cast<int*>(rec + R::G + DK * 4) = over;
+        // the next chunk's inputs load while this one is processed
+        {
+            const int nx = idx + (int)gridDim.x;
+            issue(nx < total ? nx : idx);
+        }
+
+        // ---------------- A = strict_lower(E Kh^T) (fp32), P = lower(Qs Kh^T) (f16)
+        constexpr int NLT = NB * (NB + 1) / 2;
+        static_assert((2 * NLT) % (NT / 64) == 0, "A/P tasks per wave");
+#pragma unroll
+        for (int s2 = 0; s2 < 2 * NLT / (NT / 64); ++s2) {
+            const int task = wave + (NT / 64) * s2;
+            const int which = task / NLT;
+            int t = task % NLT, mt = 0;
+            while (t > mt) { t -= mt + 1; ++mt; }
+            const int nt = t;
+            const _Float16* xa = (which == 0 ? sE + (16 * mt + r16) * LDE : sK + (16 * nt + r16) * LDE) + 2 * g4;
+            const _Float16* yb = (which == 0 ? sK + (16 * nt + r16) * LDE : sQ + (16 * mt + r16) * LDE) + 2 * g4;
+            half8 fa[NKK], fb[NKK];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                fa[kk] = ld_h8(xa + 32 * kk);
+                fb[kk] = ld_h8(yb + 32 * kk);
+            }
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) acc = mfma32(fa[kk], fb[kk], acc);
+            if (which == 0) {
+                floatx4 a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + g4 + i, c = 16 * nt + r16;
+                    a[i] = c < r ? acc[i] : 0.f;
+                    sA[r * LDA + c] = a[i];
+                }
+                // diagonal blocks also transposed: sAd[blk][col][row]
+                if (mt == nt) *reinterpret_cast<floatx4*>(sAd + (mt * 16 + r16) * LDD + g4) = a;
+            } else {
+                // P^T tile (s = 16 nt + .., t = 16 mt + ..): lane holds P[16mt + r16][16nt + g4 + i]
+                const int tr = 16 * mt + r16;
+                floatx4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (16 * nt + g4 + i <= tr) ? acc[i] : 0.f;
+                *reinterpret_cast<half4*>(sP + tr * LDT + 16 * nt + g4) = to_h4(v);
+            }
+        }
+        lds_barrier();
+        if (wave == 0) {
+            // diagonal 16x16 blocks of T: right-looking forward substitution in fp32,
+            // lane (blk, column jc), the columns of A streamed from the transposed copy
+            const int blk = lane >> 4, jc = lane & 15;
+            const float* ad = sAd + blk * 16 * LDD;
+            floatx4 acol[2][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acol[0][q] = *reinterpret_cast<const floatx4*>(ad + 4 * q);
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 15; ++m) {
+                if (m + 1 < 15) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acol[(m + 1) & 1][q] = *reinterpret_cast<const floatx4*>(ad + (m + 1) * LDD + 4 * q);
+                }
+                const float xm = x[m];
+#pragma unroll
+                for (int r = m + 1; r < 16; ++r) x[r] -= acol[m & 1][r >> 2][r & 3] * xm;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDT + 16 * blk + jc] = (_Float16)x[r];
+        } else {
+            // meanwhile: fragments of P (K = tokens) and Kh^T (K = tokens)
+            constexpr int NPB = NB * (C / 32), NKB = (DK / 16) * (C / 32);
+            for (int task = wave - 1; task < NPB + NKB; task += NT / 64 - 1) {
+                if (task < NPB) {
+                    const int rt = task / (C / 32), kk = task % (C / 32);
+                    const _Float16* src = sP + (16 * rt + r16) * LDT + 32 * kk + g4;
+                    *reinterpret_cast<half8*>(rec + R::P + ((size_t)(rt * (C / 32) + kk) * 64 + lane) * 16) =
+                        cat8(ld_h4(src), ld_h4(src + 16));
+                } else {
+                    const int tk = task - NPB, mt = tk / (C / 32), kk = tk % (C / 32);
+                    const _Float16* src = sK + (32 * kk + g4) * LDE + 16 * mt + r16;
+                    *reinterpret_cast<half8*>(rec + R::K + ((size_t)(mt * (C / 32) + kk) * 64 + lane) * 16) =
+                        cat8(ld_col4(src, LDE), ld_col4(src + 16 * LDE, LDE));
+                }
+            }
+        }
+        lds_barrier();
+        // ---------------- off-diagonal blocks by doubling: T_BA = -T_BB (A_BA T_AA)
+#pragma unroll
+        for (int sz = 16; sz < C; sz *= 2) {
+            const int nsub = sz / 16, ntask = (C / (2 * sz)) * nsub * nsub;
+            for (int task = wave; task < ntask; task += NT / 64) {
+                const int pr = task / (nsub * nsub), mi = (task / nsub) % nsub, ni = task % nsub;
+                const int a0 = 2 * sz * pr, b0 = a0 + sz;
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int k = 0; k < sz; k += 16) {
+                    const floatx4 av = *reinterpret_cast<const floatx4*>(sA + (b0 + 16 * mi + r16) * LDA + a0 + k + g4);
+                    acc = mfma16(to_h4(av), ld_col4(sT + (a0 + k + g4) * LDT + a0 + 16 * ni + r16, LDT), acc);
+                }
+                // Z^T[col][row]
+                *reinterpret_cast<half4*>(sZ + (pr * sz + 16 * ni + r16) * LDT + 16 * mi + g4) = to_h4(acc);
+            }
+            lds_barrier();
+            for (int task = wave; task < ntask; task += NT / 64) {
+                const int pr = task / (nsub * nsub), mi = (task / nsub) % nsub, ni = task % nsub;
+                const int a0 = 2 * sz * pr, b0 = a0 + sz;
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int k = 0; k < sz; k += 16)
+                    acc = mfma16(ld_h4(sT + (b0 + 16 * mi + r16) * LDT + b0 + k + g4),
+                                 ld_h4(sZ + (pr * sz + 16 * ni + r16) * LDT + k + g4), acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sT[(b0 + 16 * mi + g4 + i) * LDT + a0 + 16 * ni + r16] = (_Float16)(-acc[i]);
+            }
+            lds_barrier();
+        }
+        // ---------------- W^T = E^T T^T (fragments of W out, W^T kept) and Ũ = T X.
+        // T's upper tiles are zero, so every product runs over the full K = C.
+        static_assert((NB * NKK) % (NT / 64) == 0 && (NST * (C / 32)) % (NT / 64) == 0, "tasks per wave");
+#pragma unroll
+        for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
+            const int task = wave + (NT / 64) * s2;
+            const int rt = task / NKK, kk = task % NKK;
+            half4 fx[2][NB], fy[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                fy[k] = ld_h4(sT + (16 * rt + r16) * LDT + 16 * k + g4);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4(sEt + (32 * kk + 16 * h + r16) * LDT + 16 * k + g4);
+            }
+            floatx4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+            *reinterpret_cast<half8*>(rec + R::W + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) =
+                cat8(to_h4(acc[0]), to_h4(acc[1]));
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sWt[(32 * kk + 16 * h + g4 + i) * LDT + 16 * rt + r16] = (_Float16)acc[h][i];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < NST * (C / 32) / (NT / 64); ++s2) {
+            const int task = wave + (NT / 64) * s2;
+            const int nt = task / (C / 32), kk = task % (C / 32);
+            half4 fx[2][NB], fy[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                fy[k] = ld_h4(sXt + (16 * nt + r16) * LDT + 16 * k + g4);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4(sT + (16 * (2 * kk + h) + r16) * LDT + 16 * k + g4);
+            }
+            floatx4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+            *reinterpret_cast<half8*>(rec + R::U + ((size_t)(nt * (C / 32) + kk) * 64 + lane) * 16) =
+                cat8(to_h4(acc[0]), to_h4(acc[1]));
+        }
+        lds_barrier();
+        // ---------------- Q̃^T = Qs^T - W^T P^T (fragments of Q̃ out); P's upper tiles are zero
+#pragma unroll
+        for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
+            const int task = wave + (NT / 64) * s2;
+            const int rt = task / NKK, kk = task % NKK;
+            half4 fx[2][NB], fy[NB], fq[2];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                fy[k] = ld_h4(sP + (16 * rt + r16) * LDT + 16 * k + g4);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4(sWt + (32 * kk + 16 * h + r16) * LDT + 16 * k + g4);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) fq[h] = ld_h4(sQ + (16 * rt + r16) * LDE + 32 * kk + 16 * h + g4);
+            floatx4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+            *reinterpret_cast<half8*>(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) =
+                cat8(to_h4(f4(fq[0]) - acc[0]), to_h4(f4(fq[1]) - acc[1]));
+        }
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// pass 2: the state chain
+// ---------------------------------------------------------------------------
+// Pass 2.  One workgroup of two waves per (head, NS 16-column strips of the
+// state).  Both waves read their operand fragments straight from the
+// workspace (L2) into registers two chunks ahead of use (two register sets,
+// used alternately):
+//   wave 0 (state):  S' = diag(gamma) S, publishes f16 S' fragments in LDS,
+//                    Y = W S', U = Ũ - Y, S = S' + Kh^T U;
+//   wave 1 (output): O = P Ũ + Q̃ S' for the same chunk, and pulls a share of
+//                    the chunks further ahead into L2 (one dword per 128-byte
+//                    line; the workgroups of a head split the lines).
+// The S' fragments are double-buffered, so one barrier per chunk suffices.
+template <int DK, int DV, int NS>
+struct StateFrags {
+    half8 fw[DK / 32][C / 16], fk[DK / 16][C / 32], ur[NS][C / 32];
+    floatx4 gm[DK / 16];
+    int flag;
+};
+template <int DK, int NS>
+struct OutFrags {
+    half8 fq[DK / 32][C / 16], fp[C / 16][C / 32], ur[NS][C / 32];
+    int flag;
+};
+
+template <int DK, int DV, int NS>
+__global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsigned char* ws) {
+    using R = Rec<DK, DV>;
+    constexpr int NGRP = DV / (16 * NS), NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
+    __shared__ __align__(16) half8 sSF[2][NS][NKK][64];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lid / NGRP, ng = lid % NGRP;          // strips NS*ng .. NS*ng+NS-1
+    const int NC = p.T / C;
+    const unsigned char* rec0 = ws + (size_t)bh * NC * R::bytes;
+    const int n_l = lane & 15, g4 = 4 * (lane >> 4);
+    auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
+    };
+    auto recp = [&](int c) __attribute__((always_inline)) {
+        return rec0 + (size_t)(c < NC ? c : NC - 1) * R::bytes;
+    };
+
+    if (wave == 1) {
+        // ------------------------------------------------ output wave
+        using F = OutFrags<DK, NS>;
+        F fa, fb;
+        auto fetch = [&](int c, F& f) __attribute__((always_inline)) {
+            const unsigned char* rec = recp(c);
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt) f.fq[kk][rt] = frag(rec, R::Q + (size_t)(rt * NKK + kk) * 1024);
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+                for (int kk = 0; kk <= rt / 2; ++kk) f.fp[rt][kk] = frag(rec, R::P + (size_t)(rt * NK2 + kk) * 1024);
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int kk = 0; kk < NK2; ++kk)
+                    f.ur[s][kk] = frag(rec, R::U + (size_t)((NS * ng + s) * NK2 + kk) * 1024);
+            f.flag = *reinterpret_cast<const int*>(rec + R::G + DK * 4);
+        };
+        // L2 prefetch of this workgroup's share of the record's lines; the values
+        // are folded two chunks later (never waited on while in flight)
+        constexpr int NLINE = (int)(R::bytes / 128);
+        constexpr int LPL = (NLINE + 64 * NGRP - 1) / (64 * NGRP);
+        uint32_t tacc = 0, ta[LPL] = {}, tb[LPL] = {};
+        auto touch = [&](int c, uint32_t (&tr)[LPL]) __attribute__((always_inline)) {
+            const unsigned char* rec = recp(c);
+#pragma unroll
+            for (int r = 0; r < LPL; ++r) {
+                tacc ^= tr[r];
+                const int li = ng + NGRP * (lane + 64 * r);
+                tr[r] = *reinterpret_cast<const uint32_t*>(rec + (size_t)(li < NLINE ? li : NLINE - 1) * 128);
+            }
+        };
+        constexpr int TD = 5;
+        if (NC > 0) {
+            touch(2, ta);
+            touch(3, tb);
+            fetch(0, fa);
+            fetch(1, fb);
+        }
+        bool poisoned = false;
+        auto step = [&](int c, F& f, uint32_t (&tr)[LPL]) __attribute__((always_inline)) {
+            if (f.flag) poisoned = true;
+            floatx4 O[NS][NB];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt) {
+                    O[s][rt] = zero4();
+#pragma unroll
+                    for (int kk = 0; kk <= rt / 2; ++kk) O[s][rt] = mfma32(f.fp[rt][kk], f.ur[s][kk], O[s][rt]);
+                }
+            lds_barrier();                                   // S' of chunk c is published
+            half8 sf[NS][NKK];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) sf[s][kk] = sSF[c & 1][s][kk][lane];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) O[s][rt] = mfma32(f.fq[kk][rt], sf[s][kk], O[s][rt]);
+            fetch(c + 2, f);                                 // operands two chunks ahead
+            touch(c + TD, tr);
+            const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt) {
+                    floatx4 o = O[s][rt];
+                    if (poisoned) o = o * __builtin_nanf("");
+                    const size_t base = (tok0 + 16 * rt + g4) * DV + 16 * (NS * ng + s) + n_l;
+                    if (p.flags & GDR_OUT_BF16) {
+                        uint16_t* op = reinterpret_cast<uint16_t*>(p.o);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = f32_to_bf16(o[i]);
+                    } else {
+                        float* op = reinterpret_cast<float*>(p.o);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = o[i];
+                    }
+                }
+        };
+        for (int c = 0; c < NC; c += 2) {
+            step(c, fa, ta);
+            if (c + 1 < NC) step(c + 1, fb, tb);
+        }
+#pragma unroll
+        for (int r = 0; r < LPL; ++r) tacc ^= ta[r] ^ tb[r];
+        // never true (flag bit 31 is rejected by the API); keeps the touch loads
+        if ((p.flags & 0x80000000u) && tacc == 0x12345u) p.Sf[0] = 0.f;
+        return;
+    }
+
+    // ---------------------------------------------------- state wave
+    using F = StateFrags<DK, DV, NS>;
+    floatx4 S[NS][NKT];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[s][mt][i] = p.S0 ? p.S0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] : 0.f;
+    F fa, fb;
+    auto fetch_g = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) f.gm[mt] = *reinterpret_cast<const floatx4*>(rec + R::G + (16 * mt + g4) * 4);
+        f.flag = *reinterpret_cast<const int*>(rec + R::G + DK * 4);
+    };
+    auto fetch_w = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) f.fw[kk][rt] = frag(rec, R::W + (size_t)(rt * NKK + kk) * 1024);
+    };
+    auto fetch_u = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk) f.ur[s][kk] = frag(rec, R::U + (size_t)((NS * ng + s) * NK2 + kk) * 1024);
+    };
+    auto fetch_k = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk) f.fk[mt][kk] = frag(rec, R::K + (size_t)(mt * NK2 + kk) * 1024);
+    };
+    if (NC > 0) {
+        fetch_g(0, fa); fetch_w(0, fa); fetch_u(0, fa); fetch_k(0, fa);
+        fetch_g(1, fb); fetch_w(1, fb); fetch_u(1, fb); fetch_k(1, fb);
+    }
+    bool poisoned = false;
+    auto step = [&](int c, F& f) __attribute__((always_inline)) {
+        if (p.states) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        p.states[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] = S[s][mt][i];
+        }
+        if (f.flag) poisoned = true;
+        // S' = diag(gamma) S and its f16 fragments (K = channels), published for the output wave
+        half8 sf[NS][NKK];
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int s = 0; s < NS; ++s) S[s][mt] = S[s][mt] * f.gm[mt];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                sf[s][kk] = cat8(to_h4(S[s][2 * kk]), to_h4(S[s][2 * kk + 1]));
+                sSF[c & 1][s][kk][lane] = sf[s][kk];
+            }
+        fetch_g(c + 2, f);
+        lds_barrier();
+        // Y = W S'
+        floatx4 Y[NS][NB];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) Y[s][rt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) Y[s][rt] = mfma32(f.fw[kk][rt], sf[s][kk], Y[s][rt]);
+        fetch_w(c + 2, f);
+        // U = Ũ - W S' as B fragments (K = tokens)
+        half8 uf[NS][NK2];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk)
+                uf[s][kk] = cat8(to_h4(f4(lo4(f.ur[s][kk])) - Y[s][2 * kk]),
+                                 to_h4(f4(hi4(f.ur[s][kk])) - Y[s][2 * kk + 1]));
+        fetch_u(c + 2, f);
+        // S = S' + Kh^T U
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) S[s][mt] = mfma32(f.fk[mt][kk], uf[s][kk], S[s][mt]);
+        fetch_k(c + 2, f);
+    };
+    for (int c = 0; c < NC; c += 2) {
+        step(c, fa);
+        if (c + 1 < NC) step(c + 1, fb);
+    }
+    if (p.Sf) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.Sf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] =
+                        poisoned ? __builtin_nanf("") : S[s][mt][i];
+    }
+}
+
+constexpr int kChainStrips = 1;
+
+template <int DK, int DV, bool AS, bool BS, bool WS>
+static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
+    using LP = PrepLayout<DK, DV>;
+    auto kp = wy_kernel<DK, DV, AS, BS, WS>;
+    auto ks = chain_kernel<DK, DV, kChainStrips>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::bytes);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    const int total = p.BH * (p.T / C);
+    int ncu = 256;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int n = 0;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                ncu = n;
+        }
+    }
+    const int gp = total < ncu ? total : ncu;
+    hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(NT), LP::bytes, st, p,
+                       reinterpret_cast<unsigned char*>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ks, dim3((unsigned)(p.BH * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
+                       reinterpret_cast<const unsigned char*>(ws));
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st) {
+    const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
+    const int m = (as ? 4 : 0) | (bs ? 2 : 0) | (wsc ? 1 : 0);
+    switch (m) {
+        case 0: return launch_t<DK, DV, false, false, false>(p, ws, st);
+        case 1: return launch_t<DK, DV, false, false, true>(p, ws, st);
+        case 2: return launch_t<DK, DV, false, true, false>(p, ws, st);
+        case 3: return launch_t<DK, DV, false, true, true>(p, ws, st);
+        case 4: return launch_t<DK, DV, true, false, false>(p, ws, st);
+        case 5: return launch_t<DK, DV, true, false, true>(p, ws, st);
+        case 6: return launch_t<DK, DV, true, true, false>(p, ws, st);
+        default: return launch_t<DK, DV, true, true, true>(p, ws, st);
+    }
+}
+
+}  // namespace wy
+
+bool fwd_wy_supported(int dk, int dv, int chunk, uint32_t flags) {
+    if (flags & (GDR_ACT_F32 | GDR_FWD_GENERIC)) return false;
+    if (chunk != 64) return false;
+    return (dk == 128 || dk == 64) && (dv == 128 || dv == 64);
+}
+
+size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv) {
+    size_t rec = 0;
+    if (dk == 128 && dv == 128) rec = wy::Rec<128, 128>::bytes;
+    else if (dk == 64 && dv == 64) rec = wy::Rec<64, 64>::bytes;
+    else if (dk == 128 && dv == 64) rec = wy::Rec<128, 64>::bytes;
+    else if (dk == 64 && dv == 128) rec = wy::Rec<64, 128>::bytes;
+    return (size_t)BH * (size_t)(T / wy::C) * rec;
+}
+
+hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st) {
+    if (p.T == 0) return hipErrorInvalidValue;
+    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128>(p, ws, st);
+    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64>(p, ws, st);
+    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64>(p, ws, st);
+    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128>(p, ws, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

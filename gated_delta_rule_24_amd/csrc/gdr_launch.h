@@ -51,6 +51,12 @@ bool fwd_supported(int dk, int dv, int chunk, uint32_t flags);
 bool fwd_pipe_supported(int dk, int dv, int chunk, uint32_t flags);
 hipError_t launch_fwd_pipe(const FwdParams& p, int dk, int dv, hipStream_t st);
 
+// Two-pass path (chunk-parallel WY operands into a workspace, then the state
+// chain): bf16 activations, chunk 64, d_k and d_v in {64, 128}, T > 0.
+bool fwd_wy_supported(int dk, int dv, int chunk, uint32_t flags);
+size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv);
+hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st);
+
 struct BwdParams {
     const void* q;
     const void* k;

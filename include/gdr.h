@@ -21,8 +21,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The
- *   library never allocates device memory, never frees caller memory, and
- *   keeps no state besides a lazily cached device-property record.
+ *   library never allocates device memory (scratch space is passed in as a
+ *   caller-owned workspace), never frees caller memory, and keeps no state
+ *   besides a lazily cached device-property record.
  * - Execution is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL is the default stream).  No call synchronises.
  * - Arguments are validated before any launch.  An invalid argument returns
@@ -73,7 +74,7 @@ typedef enum gdr_status {
                                     pipelined one applies (same results up to rounding
                                     order; for testing)                               */
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 int gdr_abi_version(void);
 const char* gdr_status_string(gdr_status s);
@@ -97,14 +98,27 @@ const char* gdr_status_string(gdr_status s);
  *   chunk      : 16, 32 or 64; T must be a multiple of chunk.  The chunk is
  *                a blocking choice: results equal the token recurrence up to
  *                rounding for every chunk size.
+ *   workspace  : optional device scratch owned by the caller, contents on
+ *                entry ignored.  When it is non-NULL and
+ *                gdr_chunk_fwd_workspace_bytes() is non-zero for the call, the
+ *                two-pass path runs: every chunk's state-independent operands
+ *                are first computed in parallel into the workspace, then a
+ *                short per-head state chain consumes them.  workspace_bytes
+ *                below the required size returns GDR_ERR_WORKSPACE.  With a
+ *                NULL workspace (or a zero requirement) a single fused kernel
+ *                runs.  Both paths give the same result up to rounding.
  * Supported: d_k, d_v in {16, 32, 64, 128}; B*H >= 1; T >= 0 (T == 0 copies
  * S0 to S_final).  Returns GDR_ERR_UNSUPPORTED for other head sizes.
  */
+size_t gdr_chunk_fwd_workspace_bytes(int B, int H, int T, int d_k, int d_v,
+                                     int chunk, uint32_t flags);
+
 gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* log_alpha, const void* b, const void* w,
                          const float* S0, void* o, float* S_final,
                          int B, int H, int T, int d_k, int d_v, int chunk,
-                         uint32_t flags, void* stream);
+                         uint32_t flags, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * One recurrent decode step for N independent sequences (constant memory:

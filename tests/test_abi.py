@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == 2
     for s in range(6):
         assert len(lib.gdr_status_string(s)) > 0
     assert lib.gdr_status_string(99) == b"unknown status"
@@ -57,7 +57,8 @@ def _fwd(lib, **kw):
     args.update(kw)
     return lib.gdr_chunk_fwd(args["q"], args["k"], args["v"], args["la"], args["b"], args["w"],
                              args["S0"], args["o"], args["Sf"], args["B"], args["H"], args["T"],
-                             args["dk"], args["dv"], args["chunk"], args["flags"], None)
+                             args["dk"], args["dv"], args["chunk"], args["flags"], args.get("ws"),
+                             args.get("nbytes", 0), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -68,6 +69,20 @@ def _fwd(lib, **kw):
 ])
 def test_fwd_argument_validation(kw, status):
     assert _fwd(_lib(), **kw) == status
+
+
+def test_fwd_workspace_query_and_validation():
+    lib = _lib()
+    one = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0)
+    assert one > 3 * 64 * 128 * 2          # at least W, Q and Kh of one chunk in f16
+    assert lib.gdr_chunk_fwd_workspace_bytes(2, 3, 256, 128, 128, 64, 0) == 2 * 3 * 4 * one
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0x1) == 0   # fp32: fused only
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 32, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 32, 32, 64, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 0, 128, 128, 64, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0x20) == 0  # forced fused
+    assert _fwd(lib, ws=A, nbytes=one - 1) == 3
+    assert _fwd(lib, ws=MIS, nbytes=one) == 1
 
 
 def test_decode_argument_validation():

