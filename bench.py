@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the gated delta rule hot path on one MI355X.
 
-Headline: the chunkwise Gated DeltaNet-2 forward (gate prep, intra-chunk WY,
-inter-chunk state pass and output, fused in one kernel) at B=2, H=16,
-T=8192, d_k=d_v=128, chunk 64, bf16 activations, fp32 log-decay and state.
-One step = one gdr_chunk_fwd call over that batch, inputs resident in HBM.
+Headline: the chunkwise Gated DeltaNet-2 forward (gate prep and intra-chunk
+WY operands for all chunks in parallel, then the inter-chunk state pass with
+the output) at B=2, H=16, T=8192, d_k=d_v=128, chunk 64, bf16 activations,
+fp32 log-decay and state.  One step = one gdr_chunk_fwd call over that batch
+(two kernel launches, with a workspace), inputs resident in HBM.
 value = B*H*T head-tokens per second of wall time over the timed steps.
 
 Also reported in the same JSON line: the recurrent decode step (256
 sequences x 32 heads, fp32 state streamed in place) in GB/s, the backward
-when the library supports it, the roofline position of the forward kernel
-(algorithmic HBM bytes per launch over the measured launch duration), and
-the fp64 CPU oracle timed on this host as a reference baseline.
+(1 x 32 heads x 16384 tokens), the roofline position of the forward call
+(the method's algorithmic HBM bytes per call over the measured call
+duration, with the measured HBM traffic of both kernels), and the fp64 CPU
+oracle timed on this host as a reference baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -49,8 +51,6 @@ FWD_FLOPS_PER_TOKEN = 6 * FD * FD + 2 * FC * (3 * FD + 2 * FD)
 DN, DH, DD = 256, 32, 128
 DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + DD * 2) + DD * 4
 
-# the timed launch runs the pipelined kernel; the counters in the traffic summary
-# are only used while these sources are unchanged
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
 # head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
 # d log-decay, db, dv, dw fp32; plus S0 read and dS0 written per head
@@ -58,7 +58,10 @@ BB, BH_, BT = 1, 32, 16384
 BWD_BYTES_PER_TOKEN = 6 * FD * 2 + FD * 4 + 6 * FD * 4
 BWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
 
-FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_pipe.hip",
+# the timed call runs the two-pass kernels (WY operands, then the state chain);
+# the counters in the traffic summary are only used while these sources are
+# unchanged
+FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_wy.hip",
                       "gated_delta_rule_24_amd/csrc/gdr_device.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
 
@@ -292,6 +295,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
+            "scope": "one gdr_chunk_fwd call: wy_kernel + chain_kernel",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

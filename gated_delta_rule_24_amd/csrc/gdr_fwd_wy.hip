@@ -87,6 +87,14 @@ __device__ __forceinline__ floatx4 mfma32(half8 a, half8 b, floatx4 c) {
 }
 __device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
 __device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+// four halves from a 4-byte aligned address, as two 4-byte reads
+__device__ __forceinline__ half4 ld_h4w(const _Float16* p) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = *reinterpret_cast<const h2*>(p), b = *reinterpret_cast<const h2*>(p + 2);
+    half4 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    return r;
+}
 // four K values of a column (stride ld)
 __device__ __forceinline__ half4 ld_col4(const _Float16* p, int ld) {
     half4 h;
@@ -99,8 +107,11 @@ __device__ __forceinline__ half4 ld_col4(const _Float16* p, int ld) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 struct PrepLayout {
+    static constexpr int NT = 256;          // threads per workgroup
     static constexpr int LDE = DK + 8;      // E, Qs, Kh rows        [C][LDE]  f16
     static constexpr int LDT = C + 8;       // token-contiguous rows  [*][LDT]  f16
+    static constexpr int LDT2 = C + 2;      // E^T and X^T rows (odd dword stride: their
+                                            // transposed writes spread over the banks)
     static constexpr int LDA = C + 4;       // A                      [C][LDA]  fp32
     static constexpr int CO = DK / 8;       // key-side channel octets per row
     static constexpr int NPART = NT / CO;   // token parts of the key-side mapping
@@ -111,14 +122,18 @@ struct PrepLayout {
     static constexpr size_t oE = 0;
     static constexpr size_t oQ = oE + (size_t)C * LDE * 2;
     static constexpr size_t oK = oQ + (size_t)C * LDE * 2;
-    static constexpr size_t oEt = oK + (size_t)C * LDE * 2;     // E^T  [DK][LDT]
-    static constexpr size_t oXt = oEt + (size_t)DK * LDT * 2;   // X^T  [DV][LDT]
-    static constexpr size_t oWt = oXt + (size_t)DV * LDT * 2;   // W^T  [DK][LDT]
-    static constexpr size_t oT = oWt + (size_t)DK * LDT * 2;    // T    [C][LDT]
+    static constexpr size_t oEt = oK + (size_t)C * LDE * 2;     // E^T  [DK][LDT2]
+    static constexpr size_t oXt = oEt + (size_t)DK * LDT2 * 2;  // X^T  [DV][LDT2]
+    static constexpr size_t oT = (oXt + (size_t)DV * LDT2 * 2 + 15) & ~size_t(15);   // T [C][LDT]
     static constexpr size_t oP = oT + (size_t)C * LDT * 2;      // P    [C][LDT]
     static constexpr size_t oZ = oP + (size_t)C * LDT * 2;      // Z^T  [C/2][LDT]
     static constexpr size_t oA = oZ + (size_t)(C / 2) * LDT * 2;
     static constexpr size_t oTot = oA + (size_t)C * LDA * 4;    // [NPART][DK] fp32
+    // W^T [DK][LDT] reuses the space of A and the prefix partials: it is written
+    // after the last read of A (the doubling) and read before the next chunk's
+    // prefix is written
+    static constexpr size_t oWt = oA;
+    static_assert((size_t)DK * LDT * 2 <= (size_t)C * LDA * 4 + (size_t)NPART * DK * 4, "W^T alias");
     static constexpr int LDD = 20;                               // diagonal blocks of A, transposed
     static constexpr size_t oAd = oTot + (size_t)NPART * DK * 4; // [C/16][16][LDD] fp32
     static constexpr size_t oFl = oAd + (size_t)(C / 16) * 16 * LDD * 4;   // [NT/64] int
@@ -126,12 +141,13 @@ struct PrepLayout {
 };
 
 template <int DK, int DV, bool AS, bool BS, bool WS>
-__global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* ws) {
+__global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdParams p, unsigned char* ws) {
     using L = PrepLayout<DK, DV>;
+    constexpr int NT = L::NT, NW = NT / 64;
     using R = Rec<DK, DV>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     static_assert(L::NPART >= 1 && L::TPP >= 1 && L::XTP >= 1, "mapping");
-    constexpr int LDE = L::LDE, LDT = L::LDT, LDA = L::LDA;
+    constexpr int LDE = L::LDE, LDT = L::LDT, LDT2 = L::LDT2, LDA = L::LDA;
     constexpr int CO = L::CO, TPP = L::TPP, VO = L::VO, XTP = L::XTP;
     constexpr int NB = C / 16, NKK = DK / 32, NST = DV / 16;
 
@@ -295,7 +311,7 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
                     h2 v;
                     v[0] = et[i][j];
                     v[1] = et[i][j + 1];
-                    *reinterpret_cast<h2*>(sEt + (8 * co + i) * LDT + part * TPP + j) = v;
+                    *reinterpret_cast<h2*>(sEt + (8 * co + i) * LDT2 + part * TPP + j) = v;
                 }
             _Float16 xt[8][XTP];
 #pragma unroll
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
                     h2 v;
                     v[0] = xt[i][j];
                     v[1] = xt[i][j + 1];
-                    *reinterpret_cast<h2*>(sXt + (8 * vo + i) * LDT + xpart * XTP + j) = v;
+                    *reinterpret_cast<h2*>(sXt + (8 * vo + i) * LDT2 + xpart * XTP + j) = v;
                 }
         }
         {
@@ -341,10 +357,10 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
 
         // ---------------- A = strict_lower(E Kh^T) (fp32), P = lower(Qs Kh^T) (f16)
         constexpr int NLT = NB * (NB + 1) / 2;
-        static_assert((2 * NLT) % (NT / 64) == 0, "A/P tasks per wave");
 #pragma unroll
-        for (int s2 = 0; s2 < 2 * NLT / (NT / 64); ++s2) {
-            const int task = wave + (NT / 64) * s2;
+        for (int s2 = 0; s2 < (2 * NLT + NW - 1) / NW; ++s2) {
+            const int task = wave + NW * s2;
+            if (task >= 2 * NLT) break;
             const int which = task / NLT;
             int t = task % NLT, mt = 0;
             while (t > mt) { t -= mt + 1; ++mt; }
@@ -455,7 +471,7 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
         }
         // ---------------- W^T = E^T T^T (fragments of W out, W^T kept) and Ũ = T X.
         // T's upper tiles are zero, so every product runs over the full K = C.
-        static_assert((NB * NKK) % (NT / 64) == 0 && (NST * (C / 32)) % (NT / 64) == 0, "tasks per wave");
+        static_assert((NB * NKK) % NW == 0 && (NST * (C / 32)) % NW == 0, "tasks per wave");
 #pragma unroll
         for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
             const int task = wave + (NT / 64) * s2;
@@ -465,7 +481,7 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
             for (int k = 0; k < NB; ++k) {
                 fy[k] = ld_h4(sT + (16 * rt + r16) * LDT + 16 * k + g4);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4(sEt + (32 * kk + 16 * h + r16) * LDT + 16 * k + g4);
+                for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4w(sEt + (32 * kk + 16 * h + r16) * LDT2 + 16 * k + g4);
             }
             floatx4 acc[2] = {zero4(), zero4()};
 #pragma unroll
@@ -487,7 +503,7 @@ __global__ __launch_bounds__(NT, 1) void wy_kernel(FwdParams p, unsigned char* w
             half4 fx[2][NB], fy[NB];
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
-                fy[k] = ld_h4(sXt + (16 * nt + r16) * LDT + 16 * k + g4);
+                fy[k] = ld_h4w(sXt + (16 * nt + r16) * LDT2 + 16 * k + g4);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) fx[h][k] = ld_h4(sT + (16 * (2 * kk + h) + r16) * LDT + 16 * k + g4);
             }
@@ -556,6 +572,8 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     using R = Rec<DK, DV>;
     constexpr int NGRP = DV / (16 * NS), NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
     __shared__ __align__(16) half8 sSF[2][NS][NKK][64];
+    constexpr int LDO = 16 * NS + 4;                    // output tile row stride (floats)
+    __shared__ __align__(16) float sO[C * LDO];         // output wave only: O tile, row-major
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
@@ -638,24 +656,31 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
                     for (int s = 0; s < NS; ++s) O[s][rt] = mfma32(f.fq[kk][rt], sf[s][kk], O[s][rt]);
             fetch(c + 2, f);                                 // operands two chunks ahead
             touch(c + TD, tr);
-            const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+            // the tile goes through LDS (this wave only) so that each lane stores
+            // four consecutive columns of a row
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
-                for (int rt = 0; rt < NB; ++rt) {
-                    floatx4 o = O[s][rt];
-                    if (poisoned) o = o * __builtin_nanf("");
-                    const size_t base = (tok0 + 16 * rt + g4) * DV + 16 * (NS * ng + s) + n_l;
-                    if (p.flags & GDR_OUT_BF16) {
-                        uint16_t* op = reinterpret_cast<uint16_t*>(p.o);
+                for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = f32_to_bf16(o[i]);
-                    } else {
-                        float* op = reinterpret_cast<float*>(p.o);
+                    for (int i = 0; i < 4; ++i) sO[(16 * rt + g4 + i) * LDO + 16 * s + n_l] = O[s][rt][i];
+            const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+            constexpr int QPR = 4 * NS;                      // column quads per row
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) op[base + (size_t)i * DV] = o[i];
-                    }
+            for (int r = 0; r < C * QPR / 64; ++r) {
+                const int e = lane + 64 * r, row = e / QPR, cq = e % QPR;
+                floatx4 o = *reinterpret_cast<const floatx4*>(sO + row * LDO + 4 * cq);
+                if (poisoned) o = o * __builtin_nanf("");
+                const size_t base = (tok0 + row) * DV + 16 * NS * ng + 4 * cq;
+                if (p.flags & GDR_OUT_BF16) {
+                    uint2 u;
+                    u.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                    u.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.o) + base) = u;
+                } else {
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(p.o) + base) = o;
                 }
+            }
         };
         for (int c = 0; c < NC; c += 2) {
             step(c, fa, ta);
@@ -809,7 +834,7 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
         }
     }
     const int gp = total < ncu ? total : ncu;
-    hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(NT), LP::bytes, st, p,
+    hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(LP::NT), LP::bytes, st, p,
                        reinterpret_cast<unsigned char*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
