@@ -149,12 +149,14 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
     p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w; p.S0 = S0;
     p.dO = dO; p.dSf = dS_final;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dla = dlog_alpha; p.db = db; p.dw = dw; p.dS0 = dS0;
-    p.states = nullptr; p.dstates = nullptr;
+    p.states = nullptr; p.dstates = nullptr; p.records = nullptr;
     p.BH = B * H; p.T = T; p.flags = flags;
     if (need > 0) {
-        const size_t half = need / 2;
-        p.states = reinterpret_cast<float*>(workspace);
-        p.dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + half);
+        const size_t sb = gdr::bwd_states_bytes(B * H, T, d_k, d_v, chunk, flags);
+        char* base = reinterpret_cast<char*>(workspace);
+        p.states = reinterpret_cast<float*>(base);
+        p.dstates = reinterpret_cast<float*>(base + sb);
+        if (need > 2 * sb) p.records = base + 2 * sb;
     }
     return from_hip(gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream));
 }

@@ -18,10 +18,12 @@
 //   dq = dQs ⊙ e^{g-g_C}        dk = dE ⊙ b ⊙ e^{g-g_C} + dKh ⊙ e^{g_C-g}
 //
 // Three launches on the caller's stream:
-//   1. the forward kernels recompute every chunk-start state into the workspace;
-//   2. dstate_kernel walks the chunks backwards carrying D (one workgroup per
-//      head and block of 32 value columns: the columns of D are independent),
-//      stores each chunk-end gradient and finally writes dS0;
+//   1. the forward kernels recompute every chunk-start state into the workspace
+//      (the two-pass forward where it applies, its records in the workspace too);
+//   2. the chunks are walked backwards carrying D (the columns of D are
+//      independent), storing each chunk-end gradient and finally dS0: with the
+//      two-pass records by the reverse chain of gdr_fwd_wy.hip, otherwise by
+//      dstate_kernel (one workgroup per head and block of 32 value columns);
 //   3. grad_kernel computes the gradients of every chunk from its S and D, one
 //      workgroup per (head, chunk), all chunks in parallel, with the value
 //      dimension reduced in a fixed order (deterministic, no atomics).
@@ -201,7 +203,7 @@ __device__ __forceinline__ void chunk_prefix(const BwdParams& p, size_t tok0, fl
         }
         *reinterpret_cast<floatx4*>(tot + rg * DK + 4 * cq) = run;
     }
-    __syncthreads();
+    lds_barrier();
     if (act) {
         floatx4 off = zero4(), gC = zero4();
         for (int g = 0; g < RGK; ++g) {
@@ -214,7 +216,7 @@ __device__ __forceinline__ void chunk_prefix(const BwdParams& p, size_t tok0, fl
         gC_out = gC;
         g0_out = gm[0];
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Chunk operands in LDS: E, Qs, Kh (row-major), gamma = e^{g_C}, P (lower,
@@ -285,7 +287,7 @@ __device__ int prep_chunk(const BwdParams& p, size_t tok0, const KeyBufs<F32>& s
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // diagonal 16x16 blocks of T by forward substitution (fp32), one lane per column
     if (wave == 0) {
         const int R = lane >> 4, j = lane & 15;
@@ -303,7 +305,7 @@ __device__ int prep_chunk(const BwdParams& p, size_t tok0, const KeyBufs<F32>& s
             for (int r = 0; r < 16; ++r) s.Tm[(16 * R + r) * LDT + 16 * R + j] = (T)x[r];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // off-diagonal blocks by doubling: T_BA = -T_BB (A_BA T_AA)
 #pragma unroll
     for (int sz = 16; sz < C; sz *= 2) {
@@ -318,7 +320,7 @@ __device__ int prep_chunk(const BwdParams& p, size_t tok0, const KeyBufs<F32>& s
             for (int i = 0; i < 4; ++i)
                 s.Z[(pr * sz + 16 * mi + m_l + i) * LDT + 16 * ni + n_l] = (T)acc[i];
         }
-        __syncthreads();
+        lds_barrier();
         for (int task = wave; task < ntask; task += NW) {
             const int pr = task / (nsub * nsub), mi = (task / nsub) % nsub, ni = task % nsub;
             const int a0 = 2 * sz * pr, b0 = a0 + sz;
@@ -329,7 +331,7 @@ __device__ int prep_chunk(const BwdParams& p, size_t tok0, const KeyBufs<F32>& s
             for (int i = 0; i < 4; ++i)
                 s.Tm[(b0 + 16 * mi + m_l + i) * LDT + a0 + 16 * ni + n_l] = (T)(-acc[i]);
         }
-        __syncthreads();
+        lds_barrier();
     }
     return over;
 }
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
                 for (int i = 0; i < 4; ++i) sD[(16 * mt + m_l + i) * LDV + 16 * nt + n_l] = (T)Dacc[s][i];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // Z = Kh D + P^T dO
         for (int task = wave; task < NB * NNT; task += NW) {
             const int mt = task / NNT, nt = task % NNT;
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sZ[(16 * mt + m_l + i) * LDV + 16 * nt + n_l] = (T)acc[i];
         }
-        __syncthreads();
+        lds_barrier();
         // dR = T^T Z
         for (int task = wave; task < NB * NNT; task += NW) {
             const int mt = task / NNT, nt = task % NNT;
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sR[(16 * mt + m_l + i) * LDV + 16 * nt + n_l] = (T)acc[i];
         }
-        __syncthreads();
+        lds_barrier();
         // D <- diag(gamma) (D + Qs^T dO - E^T dR)
 #pragma unroll
         for (int s = 0; s < NSW; ++s) {
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
                 Dacc[s] = gm * (Dacc[s] + a1 - a2);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (p.dS0) {
 #pragma unroll
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
             const int r = idx / (VB / 4), cq = idx % (VB / 4);
             st4<T>(sO + r * LDV + 4 * cq, load_act4<F32>(p.dO, (tok0 + r) * DV + col0 + 4 * cq));
         }
-        __syncthreads();
+        lds_barrier();
         // R = X - E S'  and  dU = Kh D + P^T dO
         for (int task = wave; task < 2 * NVT; task += NW) {
             const int which = task / NVT, t = task % NVT, mt = t / NNT, nt = t % NNT;
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
                 for (int i = 0; i < 4; ++i) sdU[(16 * mt + m_l + i) * LDV + 16 * nt + n_l] = (T)acc[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // U = T R  and  dR = T^T dU; dv and dw from the fp32 dR
         for (int task = wave; task < 2 * NVT; task += NW) {
             const int which = task / NVT, t = task % NVT, mt = t / NNT, nt = t % NNT;
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (w_sc && tid < C) {
             float sum = 0.f;
             for (int j = 0; j < VB; ++j) sum += sW[tid * LDW + j];
@@ -673,7 +675,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // Phi: sum over the 16 lanes of each row group (fixed butterfly order)
@@ -712,7 +714,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dQs += dP Kh; dE = dA Kh - dR S'^T; dKh += dA^T E + dP^T Qs
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -739,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
                 *reinterpret_cast<floatx4*>(sG + (rg * RPK + i) * LDG + 4 * cq) = gm[i];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // element-wise gradients; dg replaces g - g_C in sG
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (!a_sc) {
         // d log alpha_i = Phi - sum_{r<i} dg_r, per channel; NPART threads per channel
         constexpr int NPART = L::NPART, RPP = C / NPART;
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
         float sum = 0.f;
         for (int r = 0; r < RPP; ++r) sum += sG[(part * RPP + r) * LDG + ch];
         sTot[part * DK + ch] = sum;
-        __syncthreads();
+        lds_barrier();
         float off = sPhi[ch];
         for (int q = 0; q < part; ++q) off -= sTot[q * DK + ch];
         for (int r = 0; r < RPP; ++r) {
@@ -803,7 +805,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
             for (int ch = 0; ch < DK; ++ch) sum += sPhi[ch];
             sMisc[0] = sum;
         }
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {
             const float v = lane < C ? sRow[lane] : 0.f;
             float incl = v;
@@ -831,7 +833,7 @@ __global__ void copy_or_zero(float* dst, const float* src, size_t n) {
 }
 
 template <int DK, int DV, int C, bool F32>
-static hipError_t launch_t(const BwdParams& p, hipStream_t st) {
+static hipError_t launch_t(const BwdParams& p, hipStream_t st, bool with_dstate) {
     using LD = DstateLayout<DK, DV, C, F32>;
     using LG = GradLayout<DK, DV, C, F32>;
     auto kd = dstate_kernel<DK, DV, C, F32>;
@@ -847,9 +849,11 @@ static hipError_t launch_t(const BwdParams& p, hipStream_t st) {
         attr_done = true;
     }
     const int NC = p.T / C;
-    hipLaunchKernelGGL(kd, dim3((unsigned)(p.BH * (DV / VB))), dim3(LD::NT), LD::bytes, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (with_dstate) {
+        hipLaunchKernelGGL(kd, dim3((unsigned)(p.BH * (DV / VB))), dim3(LD::NT), LD::bytes, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(kg, dim3((unsigned)(p.BH * NC)), dim3(LG::NT), LG::bytes, st, p);
     return hipGetLastError();
 }
@@ -866,10 +870,18 @@ bool bwd_supported(int dk, int dv, int chunk, uint32_t /*flags*/) {
     return dk == dv && (dk == 64 || dk == 128) && (chunk == 32 || chunk == 64);
 }
 
+size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags) {
+    const int cb = bwd::bwd_chunk(chunk, flags);
+    return (size_t)BH * (size_t)(T / cb) * (size_t)dk * (size_t)dv * sizeof(float);
+}
+
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags) {
     const int cb = bwd::bwd_chunk(chunk, flags);
-    const size_t per = (size_t)BH * (size_t)(T / cb) * (size_t)dk * (size_t)dv * sizeof(float);
-    return 2 * per;   // chunk-start states, then chunk-end state gradients
+    // chunk-start states, chunk-end state gradients, and (where the two-pass forward
+    // recomputes the states) its per-chunk records
+    size_t n = 2 * bwd_states_bytes(BH, T, dk, dv, chunk, flags);
+    if (T > 0 && fwd_wy_supported(dk, dv, cb, flags)) n += fwd_wy_workspace_bytes(BH, T, dk, dv, true);
+    return n;
 }
 
 hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t st) {
@@ -888,18 +900,30 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
     f.q = p.q; f.k = p.k; f.v = p.v; f.la = p.la; f.b = p.b; f.w = p.w; f.S0 = p.S0;
     f.o = nullptr; f.Sf = nullptr; f.states = p.states;
     f.BH = p.BH; f.T = p.T; f.flags = p.flags & ~(uint32_t)GDR_OUT_BF16;
-    int used = 0;
-    hipError_t e = launch_fwd(f, dk, dv, cb, st, &used);
-    if (e != hipSuccess) return e;
-    if (used != cb) return hipErrorInvalidValue;
+    hipError_t e;
+    const bool wyp = p.records && fwd_wy_supported(dk, dv, cb, p.flags);
+    if (wyp) {
+        // two-pass forward (its records keep the operands the reverse chain needs),
+        // then the reverse chain over those records
+        e = launch_fwd_wy(f, dk, dv, p.records, st, true);
+        if (e != hipSuccess) return e;
+        e = launch_bwd_dchain(p, dk, dv, p.records, st);
+        if (e != hipSuccess) return e;
+    } else {
+        int used = 0;
+        e = launch_fwd(f, dk, dv, cb, st, &used);
+        if (e != hipSuccess) return e;
+        if (used != cb) return hipErrorInvalidValue;
+    }
     // 2 and 3
     const bool f32 = (p.flags & GDR_ACT_F32) != 0;
+    const bool ds = !wyp;
     if (dk == 128) {
-        if (f32) return bwd::launch_t<128, 128, 32, true>(p, st);
-        return cb == 64 ? bwd::launch_t<128, 128, 64, false>(p, st) : bwd::launch_t<128, 128, 32, false>(p, st);
+        if (f32) return bwd::launch_t<128, 128, 32, true>(p, st, ds);
+        return cb == 64 ? bwd::launch_t<128, 128, 64, false>(p, st, ds) : bwd::launch_t<128, 128, 32, false>(p, st, ds);
     }
-    if (f32) return bwd::launch_t<64, 64, 32, true>(p, st);
-    return cb == 64 ? bwd::launch_t<64, 64, 64, false>(p, st) : bwd::launch_t<64, 64, 32, false>(p, st);
+    if (f32) return bwd::launch_t<64, 64, 32, true>(p, st, ds);
+    return cb == 64 ? bwd::launch_t<64, 64, 64, false>(p, st, ds) : bwd::launch_t<64, 64, 32, false>(p, st, ds);
 }
 
 }  // namespace gdr

@@ -51,6 +51,14 @@ struct Rec {
     static constexpr size_t G = U + (size_t)C * DV * 2;
     static constexpr size_t bytes = G + (((size_t)DK * 4 + 16 + 255) & ~size_t(255));
     static constexpr size_t strip = (size_t)C * 16 * 2;   // Ũ bytes per 16-column strip
+    // appended when the backward consumes the records:
+    //   KW  block (rt, kk): row t = 16 rt + r of Kh, K = channels
+    //   WT  block (mt, kk): channel 16 mt + r of W^T, K = tokens
+    //   QT  block (mt, kk): channel 16 mt + r of Q̃^T, K = tokens
+    static constexpr size_t KW = bytes;
+    static constexpr size_t WT = KW + (size_t)C * DK * 2;
+    static constexpr size_t QT = WT + (size_t)C * DK * 2;
+    static constexpr size_t bwd_bytes = QT + (size_t)C * DK * 2;
 };
 
 __device__ __forceinline__ half4 to_h4(floatx4 v) {
@@ -140,7 +148,7 @@ struct PrepLayout {
     static constexpr size_t bytes = oFl + (size_t)(NT / 64) * 4;
 };
 
-template <int DK, int DV, bool AS, bool BS, bool WS>
+template <int DK, int DV, bool AS, bool BS, bool WS, bool BL>
 __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdParams p, unsigned char* ws) {
     using L = PrepLayout<DK, DV>;
     constexpr int NT = L::NT, NW = NT / 64;
@@ -230,7 +238,8 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     int idx = blockIdx.x;
     if (idx < total) issue(idx);
     for (; idx < total; idx += gridDim.x) {
-        unsigned char* rec = ws + (size_t)idx * R::bytes;
+        constexpr size_t RB = BL ? R::bwd_bytes : R::bytes;
+        unsigned char* rec = ws + (size_t)idx * RB;
         // ---------------- element-wise: in-chunk prefix, E, Qs, Kh, X (fp32 -> f16)
         float gl[TPP][8];
         {
@@ -535,8 +544,39 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             for (int k = 0; k < NB; ++k)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
-            *reinterpret_cast<half8*>(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) =
-                cat8(to_h4(f4(fq[0]) - acc[0]), to_h4(f4(fq[1]) - acc[1]));
+            const half4 q0 = to_h4(f4(fq[0]) - acc[0]), q1 = to_h4(f4(fq[1]) - acc[1]);
+            *reinterpret_cast<half8*>(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) = cat8(q0, q1);
+            if constexpr (BL) {
+                // Q̃^T [ch][t] into the (now free) E^T buffer for the channel-row fragments
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sEt[(32 * kk + g4 + i) * LDT2 + 16 * rt + r16] = q0[i];
+                    sEt[(32 * kk + 16 + g4 + i) * LDT2 + 16 * rt + r16] = q1[i];
+                }
+            }
+        }
+        if constexpr (BL) {
+            // fragments for the backward: Kh by rows (K = channels), W^T and Q̃^T by
+            // channel rows (K = tokens)
+            for (int task = wave; task < NB * NKK; task += NT / 64) {
+                const int rt = task / NKK, kk = task % NKK;
+                const _Float16* src = sK + (16 * rt + r16) * LDE + 32 * kk + g4;
+                *reinterpret_cast<half8*>(rec + R::KW + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) =
+                    cat8(ld_h4(src), ld_h4(src + 16));
+            }
+            for (int task = wave; task < (DK / 16) * (C / 32); task += NT / 64) {
+                const int mt = task / (C / 32), kk = task % (C / 32);
+                const _Float16* src = sWt + (16 * mt + r16) * LDT + 32 * kk + g4;
+                *reinterpret_cast<half8*>(rec + R::WT + ((size_t)(mt * (C / 32) + kk) * 64 + lane) * 16) =
+                    cat8(ld_h4(src), ld_h4(src + 16));
+            }
+            lds_barrier();
+            for (int task = wave; task < (DK / 16) * (C / 32); task += NT / 64) {
+                const int mt = task / (C / 32), kk = task % (C / 32);
+                const _Float16* src = sEt + (16 * mt + r16) * LDT2 + 32 * kk + g4;
+                *reinterpret_cast<half8*>(rec + R::QT + ((size_t)(mt * (C / 32) + kk) * 64 + lane) * 16) =
+                    cat8(ld_h4w(src), ld_h4w(src + 16));
+            }
         }
         lds_barrier();
     }
@@ -568,7 +608,7 @@ struct OutFrags {
 };
 
 template <int DK, int DV, int NS>
-__global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsigned char* ws) {
+__global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsigned char* ws, size_t RB) {
     using R = Rec<DK, DV>;
     constexpr int NGRP = DV / (16 * NS), NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
     __shared__ __align__(16) half8 sSF[2][NS][NKK][64];
@@ -579,13 +619,13 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
     const int bh = lid / NGRP, ng = lid % NGRP;          // strips NS*ng .. NS*ng+NS-1
     const int NC = p.T / C;
-    const unsigned char* rec0 = ws + (size_t)bh * NC * R::bytes;
+    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
     const int n_l = lane & 15, g4 = 4 * (lane >> 4);
     auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
         return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
     };
     auto recp = [&](int c) __attribute__((always_inline)) {
-        return rec0 + (size_t)(c < NC ? c : NC - 1) * R::bytes;
+        return rec0 + (size_t)(c < NC ? c : NC - 1) * RB;
     };
 
     if (wave == 1) {
@@ -611,7 +651,7 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
         };
         // L2 prefetch of this workgroup's share of the record's lines; the values
         // are folded two chunks later (never waited on while in flight)
-        constexpr int NLINE = (int)(R::bytes / 128);
+        constexpr int NLINE = (int)(R::bytes / 128);   // the forward part of a record
         constexpr int LPL = (NLINE + 64 * NGRP - 1) / (64 * NGRP);
         uint32_t tacc = 0, ta[LPL] = {}, tb[LPL] = {};
         auto touch = [&](int c, uint32_t (&tr)[LPL]) __attribute__((always_inline)) {
@@ -657,7 +697,8 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
             fetch(c + 2, f);                                 // operands two chunks ahead
             touch(c + TD, tr);
             // the tile goes through LDS (this wave only) so that each lane stores
-            // four consecutive columns of a row
+            // four consecutive columns of a row (state-only passes have no output)
+            if (p.o == nullptr) return;
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -744,7 +785,8 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
                 for (int mt = 0; mt < NKT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        p.states[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] = S[s][mt][i];
+                        p.states[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] =
+                            poisoned ? __builtin_nanf("") : S[s][mt][i];
         }
         if (f.flag) poisoned = true;
         // S' = diag(gamma) S and its f16 fragments (K = channels), published for the output wave
@@ -809,13 +851,205 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     }
 }
 
+// Reverse chain of the backward.  With the forward's chunk operands, the
+// gradient of the chunk-start state follows from the gradient D of the
+// chunk-end state as
+//   diag(e^{g_C}) (D + Q̃^T dO - W^T (Kh D)),
+// because the triangular solve of the reverse mode folds into W and Q̃
+// (E^T T^T = W^T and Qs - P W = Q̃).  One workgroup of two waves per (head,
+// 16-column strip): wave 0 carries D (Z = Kh D, D += F - W^T Z, D *= gamma)
+// and stores every chunk-end gradient; wave 1 computes F = Q̃^T dO one chunk
+// ahead (nothing on the chain depends on it) and publishes it in LDS.  Both
+// prefetch their operands two chunks ahead.
+template <int DK, int NK2>
+struct DFrags {
+    half8 kw[DK / 32][C / 16], wt[DK / 16][NK2];
+    floatx4 gm[DK / 16];
+    int flag;
+};
+template <int DK, int NK2>
+struct FFrags {
+    half8 qt[DK / 16][NK2];
+    uint32_t dob[NK2][8];       // raw bf16 dO values (K = tokens)
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsigned char* ws) {
+    using R = Rec<DK, DV>;
+    constexpr size_t RB = R::bwd_bytes;
+    constexpr int NST = DV / 16, NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
+    __shared__ __align__(16) floatx4 sF[2][NKT][64];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lid / NST, nt = lid % NST;
+    const int NC = p.T / C;
+    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
+    const int n_l = lane & 15, g4 = 4 * (lane >> 4), col = 16 * nt + n_l;
+    auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
+    };
+    auto recp = [&](int c) __attribute__((always_inline)) {
+        return rec0 + (size_t)(c < 0 ? 0 : c) * RB;
+    };
+
+    if (wave == 1) {
+        // ------------------------------------------------ F = Q̃^T dO, one chunk ahead
+        using F = FFrags<DK, NK2>;
+        const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dO);
+        auto fetch = [&](int c, F& f) __attribute__((always_inline)) {
+            const int cc = c < 0 ? 0 : c;
+            const unsigned char* rec = recp(cc);
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int kk = 0; kk < NK2; ++kk) f.qt[mt][kk] = frag(rec, R::QT + (size_t)(mt * NK2 + kk) * 1024);
+            const size_t tok0 = (size_t)bh * p.T + (size_t)cc * C;
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 32 * kk + (j < 4 ? g4 + j : 16 + g4 + j - 4);
+                    f.dob[kk][j] = dO[(tok0 + t) * DV + col];
+                }
+        };
+        auto compute = [&](F& f, int buf) __attribute__((always_inline)) {
+            half8 dof[NK2];
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dof[kk][j] = (_Float16)__uint_as_float(f.dob[kk][j] << 16);
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NK2; ++kk) acc = mfma32(f.qt[mt][kk], dof[kk], acc);
+                sF[buf][mt][lane] = acc;
+            }
+        };
+        F fa, fb;
+        if (NC > 0) {
+            fetch(NC - 1, fa);
+            fetch(NC - 2, fb);
+            compute(fa, 0);
+            fetch(NC - 3, fa);
+        }
+        // iteration j (chunk NC-1-j on wave 0) prepares chunk NC-2-j
+        auto step = [&](int j, F& f) __attribute__((always_inline)) {
+            lds_barrier();
+            const int c = NC - 2 - j;
+            if (c >= 0) {
+                compute(f, (j + 1) & 1);
+                fetch(c - 2, f);
+            }
+        };
+        for (int j = 0; j < NC; j += 2) {
+            step(j, fb);
+            if (j + 1 < NC) step(j + 1, fa);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- wave 0: D, backwards
+    using F = DFrags<DK, NK2>;
+    floatx4 D[NKT];
+#pragma unroll
+    for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            D[mt][i] = p.dSf ? p.dSf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] : 0.f;
+    auto fetch_kg = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) f.kw[kk][rt] = frag(rec, R::KW + (size_t)(rt * NKK + kk) * 1024);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) f.gm[mt] = *reinterpret_cast<const floatx4*>(rec + R::G + (16 * mt + g4) * 4);
+        f.flag = *reinterpret_cast<const int*>(rec + R::G + DK * 4);
+    };
+    auto fetch_w = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk) f.wt[mt][kk] = frag(rec, R::WT + (size_t)(mt * NK2 + kk) * 1024);
+    };
+    F fa, fb;
+    if (NC > 0) {
+        fetch_kg(NC - 1, fa); fetch_w(NC - 1, fa);
+        fetch_kg(NC - 2, fb); fetch_w(NC - 2, fb);
+    }
+    bool poisoned = false;
+    const float qnan = __builtin_nanf("");
+    auto step = [&](int j, F& f) __attribute__((always_inline)) {
+        const int c = NC - 1 - j;
+        // the gradient of this chunk's end state, for the gradient kernel
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.dstates[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + col] = poisoned ? qnan : D[mt][i];
+        if (f.flag) poisoned = true;
+        // Z = Kh D
+        half8 df[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) df[kk] = cat8(to_h4(D[2 * kk]), to_h4(D[2 * kk + 1]));
+        floatx4 Z[NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Z[rt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) Z[rt] = mfma32(f.kw[kk][rt], df[kk], Z[rt]);
+        lds_barrier();                                   // F of chunk c is published
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) D[mt] += sF[j & 1][mt][lane];
+        // D += -W^T Z, then D = diag(gamma) D
+        half8 zf[NK2];
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) zf[kk] = cat8(to_h4(-Z[2 * kk]), to_h4(-Z[2 * kk + 1]));
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt) D[mt] = mfma32(f.wt[mt][kk], zf[kk], D[mt]);
+        const floatx4* gm = f.gm;
+        floatx4 g2[NKT];
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) g2[mt] = gm[mt];
+        fetch_kg(c - 2, f);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) D[mt] = D[mt] * g2[mt];
+        fetch_w(c - 2, f);
+    };
+    for (int j = 0; j < NC; j += 2) {
+        step(j, fa);
+        if (j + 1 < NC) step(j + 1, fb);
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.dS0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] = poisoned ? qnan : D[mt][i];
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t st) {
+    hipLaunchKernelGGL((dchain_kernel<DK, DV>), dim3((unsigned)(p.BH * (DV / 16))), dim3(128), 0, st, p,
+                       reinterpret_cast<const unsigned char*>(ws));
+    return hipGetLastError();
+}
+
 constexpr int kChainStrips = 1;
 
-template <int DK, int DV, bool AS, bool BS, bool WS>
+template <int DK, int DV, bool AS, bool BS, bool WS, bool BL>
 static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
     using LP = PrepLayout<DK, DV>;
-    auto kp = wy_kernel<DK, DV, AS, BS, WS>;
+    auto kp = wy_kernel<DK, DV, AS, BS, WS, BL>;
     auto ks = chain_kernel<DK, DV, kChainStrips>;
+    constexpr size_t RB = BL ? Rec<DK, DV>::bwd_bytes : Rec<DK, DV>::bytes;
     static bool attr_done = false;
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
@@ -839,23 +1073,23 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ks, dim3((unsigned)(p.BH * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
-                       reinterpret_cast<const unsigned char*>(ws));
+                       reinterpret_cast<const unsigned char*>(ws), RB);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool BL>
 static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st) {
     const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
     const int m = (as ? 4 : 0) | (bs ? 2 : 0) | (wsc ? 1 : 0);
     switch (m) {
-        case 0: return launch_t<DK, DV, false, false, false>(p, ws, st);
-        case 1: return launch_t<DK, DV, false, false, true>(p, ws, st);
-        case 2: return launch_t<DK, DV, false, true, false>(p, ws, st);
-        case 3: return launch_t<DK, DV, false, true, true>(p, ws, st);
-        case 4: return launch_t<DK, DV, true, false, false>(p, ws, st);
-        case 5: return launch_t<DK, DV, true, false, true>(p, ws, st);
-        case 6: return launch_t<DK, DV, true, true, false>(p, ws, st);
-        default: return launch_t<DK, DV, true, true, true>(p, ws, st);
+        case 0: return launch_t<DK, DV, false, false, false, BL>(p, ws, st);
+        case 1: return launch_t<DK, DV, false, false, true, BL>(p, ws, st);
+        case 2: return launch_t<DK, DV, false, true, false, BL>(p, ws, st);
+        case 3: return launch_t<DK, DV, false, true, true, BL>(p, ws, st);
+        case 4: return launch_t<DK, DV, true, false, false, BL>(p, ws, st);
+        case 5: return launch_t<DK, DV, true, false, true, BL>(p, ws, st);
+        case 6: return launch_t<DK, DV, true, true, false, BL>(p, ws, st);
+        default: return launch_t<DK, DV, true, true, true, BL>(p, ws, st);
     }
 }
 
@@ -867,21 +1101,32 @@ bool fwd_wy_supported(int dk, int dv, int chunk, uint32_t flags) {
     return (dk == 128 || dk == 64) && (dv == 128 || dv == 64);
 }
 
-size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv) {
+size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts) {
     size_t rec = 0;
-    if (dk == 128 && dv == 128) rec = wy::Rec<128, 128>::bytes;
-    else if (dk == 64 && dv == 64) rec = wy::Rec<64, 64>::bytes;
-    else if (dk == 128 && dv == 64) rec = wy::Rec<128, 64>::bytes;
-    else if (dk == 64 && dv == 128) rec = wy::Rec<64, 128>::bytes;
+    if (dk == 128 && dv == 128) rec = bwd_layouts ? wy::Rec<128, 128>::bwd_bytes : wy::Rec<128, 128>::bytes;
+    else if (dk == 64 && dv == 64) rec = bwd_layouts ? wy::Rec<64, 64>::bwd_bytes : wy::Rec<64, 64>::bytes;
+    else if (dk == 128 && dv == 64) rec = bwd_layouts ? wy::Rec<128, 64>::bwd_bytes : wy::Rec<128, 64>::bytes;
+    else if (dk == 64 && dv == 128) rec = bwd_layouts ? wy::Rec<64, 128>::bwd_bytes : wy::Rec<64, 128>::bytes;
     return (size_t)BH * (size_t)(T / wy::C) * rec;
 }
 
-hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st) {
+hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st, bool bwd_layouts) {
     if (p.T == 0) return hipErrorInvalidValue;
-    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128>(p, ws, st);
-    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64>(p, ws, st);
-    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64>(p, ws, st);
-    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128>(p, ws, st);
+    if (bwd_layouts) {
+        if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, true>(p, ws, st);
+        if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, true>(p, ws, st);
+        return hipErrorInvalidValue;
+    }
+    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false>(p, ws, st);
+    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false>(p, ws, st);
+    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false>(p, ws, st);
+    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false>(p, ws, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st) {
+    if (dk == 128 && dv == 128) return wy::launch_dchain<128, 128>(p, records, st);
+    if (dk == 64 && dv == 64) return wy::launch_dchain<64, 64>(p, records, st);
     return hipErrorInvalidValue;
 }
 

@@ -53,9 +53,12 @@ hipError_t launch_fwd_pipe(const FwdParams& p, int dk, int dv, hipStream_t st);
 
 // Two-pass path (chunk-parallel WY operands into a workspace, then the state
 // chain): bf16 activations, chunk 64, d_k and d_v in {64, 128}, T > 0.
+// bwd_layouts: also write the fragment layouts the backward's reverse chain
+// reads (d_k == d_v only).
 bool fwd_wy_supported(int dk, int dv, int chunk, uint32_t flags);
-size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv);
-hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st);
+size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts = false);
+hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st,
+                         bool bwd_layouts = false);
 
 struct BwdParams {
     const void* q;
@@ -76,12 +79,17 @@ struct BwdParams {
     float* dS0;
     float* states;         // workspace: chunk-start states
     float* dstates;        // workspace: state gradients at chunk ends
+    void* records;         // workspace: per-chunk WY operands of the two-pass forward (or null)
     int BH;
     int T;
     uint32_t flags;
 };
 
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
+// Reverse state-gradient chain over the records of launch_fwd_wy(..., bwd_layouts = true).
+hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st);
+// split of that workspace: states, then state gradients, then the forward records
+size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
 bool bwd_supported(int dk, int dv, int chunk, uint32_t flags);
 hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t st);
 
