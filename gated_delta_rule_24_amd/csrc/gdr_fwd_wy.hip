@@ -200,31 +200,40 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 rq[TPP], rk[TPP], rb[TPP], rv[XTP], rw[XTP];
     floatx4 rla[TPP][2];
-    auto issue = [&](int idx) {
+    // The loads of a chunk are issued in three groups spread over the previous
+    // chunk's phases (q and k, then b and log alpha, then v and w), so that
+    // their transfer overlaps computation instead of stalling one issue point.
+    auto issue = [&](int idx, int group) __attribute__((always_inline)) {
         const int bh = idx / NC, c = idx % NC;
         const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+        if (group < 2) {
 #pragma unroll
-        for (int j = 0; j < TPP; ++j) {
-            const size_t t = tok0 + part * TPP + j;
-            const size_t ix = t * DK + 8 * co;
-            rq[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + ix);
-            rk[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + ix);
-            if constexpr (BS) rb[j][0] = bg[t];
-            else rb[j] = *reinterpret_cast<const u32x4*>(bg + ix);
-            if constexpr (AS) {
-                rla[j][0][0] = p.la[t];
-            } else {
-                rla[j][0] = *reinterpret_cast<const floatx4*>(p.la + ix);
-                rla[j][1] = *reinterpret_cast<const floatx4*>(p.la + ix + 4);
+            for (int j = 0; j < TPP; ++j) {
+                const size_t t = tok0 + part * TPP + j;
+                const size_t ix = t * DK + 8 * co;
+                if (group == 0) {
+                    rq[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + ix);
+                    rk[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + ix);
+                } else {
+                    if constexpr (BS) rb[j][0] = bg[t];
+                    else rb[j] = *reinterpret_cast<const u32x4*>(bg + ix);
+                    if constexpr (AS) {
+                        rla[j][0][0] = p.la[t];
+                    } else {
+                        rla[j][0] = *reinterpret_cast<const floatx4*>(p.la + ix);
+                        rla[j][1] = *reinterpret_cast<const floatx4*>(p.la + ix + 4);
+                    }
+                }
             }
-        }
+        } else {
 #pragma unroll
-        for (int j = 0; j < XTP; ++j) {
-            const size_t t = tok0 + xpart * XTP + j;
-            const size_t ix = t * DV + 8 * vo;
-            rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
-            if constexpr (WS) rw[j][0] = wg[t];
-            else rw[j] = *reinterpret_cast<const u32x4*>(wg + ix);
+            for (int j = 0; j < XTP; ++j) {
+                const size_t t = tok0 + xpart * XTP + j;
+                const size_t ix = t * DV + 8 * vo;
+                rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
+                if constexpr (WS) rw[j][0] = wg[t];
+                else rw[j] = *reinterpret_cast<const u32x4*>(wg + ix);
+            }
         }
     };
     auto unpack8 = [](u32x4 u, float (&f)[8]) {
@@ -236,12 +245,18 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     };
 
     int idx = blockIdx.x;
-    if (idx < total) issue(idx);
+    if (idx < total) {
+        issue(idx, 0);
+        issue(idx, 1);
+        issue(idx, 2);
+    }
     for (; idx < total; idx += gridDim.x) {
+        const int nx = idx + (int)gridDim.x < total ? idx + (int)gridDim.x : idx;
         constexpr size_t RB = BL ? R::bwd_bytes : R::bytes;
         unsigned char* rec = ws + (size_t)idx * RB;
         // ---------------- element-wise: in-chunk prefix, E, Qs, Kh, X (fp32 -> f16)
         float gl[TPP][8];
+        floatx4 off[2];
         {
             float run[8];
 #pragma unroll
@@ -253,21 +268,37 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                     run[i] += (AS ? rla[j][0][0] : rla[j][i >> 2][i & 3]) * kLog2e;
                     gl[j][i] = run[i];
                 }
-            floatx4 r0, r1;
+            // prefix over the token parts: within the wave across the lane groups
+            // (lanes CO apart hold the same channels), then over the waves in LDS
+            float inc[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { r0[i] = run[i]; r1[i] = run[4 + i]; }
-            *reinterpret_cast<floatx4*>(sTot + part * DK + 8 * co) = r0;
-            *reinterpret_cast<floatx4*>(sTot + part * DK + 8 * co + 4) = r1;
+            for (int i = 0; i < 8; ++i) inc[i] = run[i];
+#pragma unroll
+            for (int sh = CO; sh < 64; sh *= 2)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float t = __shfl_up(inc[i], sh);
+                    if (lane >= sh) inc[i] += t;
+                }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) off[i >> 2][i & 3] = inc[i] - run[i];
+            if (lane >= 64 - CO) {
+                floatx4 r0, r1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { r0[i] = inc[i]; r1[i] = inc[4 + i]; }
+                *reinterpret_cast<floatx4*>(sTot + wave * DK + 8 * co) = r0;
+                *reinterpret_cast<floatx4*>(sTot + wave * DK + 8 * co + 4) = r1;
+            }
         }
         lds_barrier();
         int over = 0;
         {
-            floatx4 off[2] = {zero4(), zero4()}, gC[2] = {zero4(), zero4()};
+            floatx4 gC[2] = {zero4(), zero4()};
 #pragma unroll
-            for (int q = 0; q < L::NPART; ++q) {
-                const floatx4 t0 = *reinterpret_cast<const floatx4*>(sTot + q * DK + 8 * co);
-                const floatx4 t1 = *reinterpret_cast<const floatx4*>(sTot + q * DK + 8 * co + 4);
-                if (q < part) { off[0] += t0; off[1] += t1; }
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const floatx4 t0 = *reinterpret_cast<const floatx4*>(sTot + w2 * DK + 8 * co);
+                const floatx4 t1 = *reinterpret_cast<const floatx4*>(sTot + w2 * DK + 8 * co + 4);
+                if (w2 < wave) { off[0] += t0; off[1] += t1; }
                 gC[0] += t0;
                 gC[1] += t1;
             }
@@ -359,33 +390,36 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
         }
         if (tid == 0) *reinterpret_cast<int*>(rec + R::G + DK * 4) = over;
         // the next chunk's inputs load while this one is processed
-        {
-            const int nx = idx + (int)gridDim.x;
-            issue(nx < total ? nx : idx);
-        }
+        issue(nx, 0);
 
         // ---------------- A = strict_lower(E Kh^T) (fp32), P = lower(Qs Kh^T) (f16)
+        // One lower tile (mt, nt) per task gives both its A and its P tile: the
+        // Kh fragments are read once and the two MFMA chains interleave.
         constexpr int NLT = NB * (NB + 1) / 2;
 #pragma unroll
-        for (int s2 = 0; s2 < (2 * NLT + NW - 1) / NW; ++s2) {
+        for (int s2 = 0; s2 < (NLT + NW - 1) / NW; ++s2) {
             const int task = wave + NW * s2;
-            if (task >= 2 * NLT) break;
-            const int which = task / NLT;
-            int t = task % NLT, mt = 0;
+            if (task >= NLT) break;
+            int t = task, mt = 0;
             while (t > mt) { t -= mt + 1; ++mt; }
             const int nt = t;
-            const _Float16* xa = (which == 0 ? sE + (16 * mt + r16) * LDE : sK + (16 * nt + r16) * LDE) + 2 * g4;
-            const _Float16* yb = (which == 0 ? sK + (16 * nt + r16) * LDE : sQ + (16 * mt + r16) * LDE) + 2 * g4;
-            half8 fa[NKK], fb[NKK];
+            const _Float16* xe = sE + (16 * mt + r16) * LDE + 2 * g4;
+            const _Float16* xq = sQ + (16 * mt + r16) * LDE + 2 * g4;
+            const _Float16* xk = sK + (16 * nt + r16) * LDE + 2 * g4;
+            half8 fe[NKK], fq[NKK], fk[NKK];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                fa[kk] = ld_h8(xa + 32 * kk);
-                fb[kk] = ld_h8(yb + 32 * kk);
+                fe[kk] = ld_h8(xe + 32 * kk);
+                fk[kk] = ld_h8(xk + 32 * kk);
+                fq[kk] = ld_h8(xq + 32 * kk);
             }
-            floatx4 acc = zero4();
+            floatx4 acc = zero4(), acp = zero4();
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = mfma32(fa[kk], fb[kk], acc);
-            if (which == 0) {
+            for (int kk = 0; kk < NKK; ++kk) {
+                acc = mfma32(fe[kk], fk[kk], acc);
+                acp = mfma32(fk[kk], fq[kk], acp);
+            }
+            {
                 floatx4 a;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -395,16 +429,18 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 }
                 // diagonal blocks also transposed: sAd[blk][col][row]
                 if (mt == nt) *reinterpret_cast<floatx4*>(sAd + (mt * 16 + r16) * LDD + g4) = a;
-            } else {
+            }
+            {
                 // P^T tile (s = 16 nt + .., t = 16 mt + ..): lane holds P[16mt + r16][16nt + g4 + i]
                 const int tr = 16 * mt + r16;
                 floatx4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (16 * nt + g4 + i <= tr) ? acc[i] : 0.f;
+                for (int i = 0; i < 4; ++i) v[i] = (16 * nt + g4 + i <= tr) ? acp[i] : 0.f;
                 *reinterpret_cast<half4*>(sP + tr * LDT + 16 * nt + g4) = to_h4(v);
             }
         }
         lds_barrier();
+        issue(nx, 1);
         if (wave == 0) {
             // diagonal 16x16 blocks of T: right-looking forward substitution in fp32,
             // lane (blk, column jc), the columns of A streamed from the transposed copy
@@ -480,6 +516,8 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
         }
         // ---------------- W^T = E^T T^T (fragments of W out, W^T kept) and Ũ = T X.
         // T's upper tiles are zero, so every product runs over the full K = C.
+        // Pairs of 16-token blocks form the 32-deep MFMA operands (both sides in
+        // the same K order).
         static_assert((NB * NKK) % NW == 0 && (NST * (C / 32)) % NW == 0, "tasks per wave");
 #pragma unroll
         for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
@@ -494,9 +532,10 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             }
             floatx4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-            for (int k = 0; k < NB; ++k)
+            for (int k = 0; k < NB; k += 2)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = mfma32(cat8(fx[h][k], fx[h][k + 1]), cat8(fy[k], fy[k + 1]), acc[h]);
             *reinterpret_cast<half8*>(rec + R::W + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) =
                 cat8(to_h4(acc[0]), to_h4(acc[1]));
 #pragma unroll
@@ -518,13 +557,15 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             }
             floatx4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-            for (int k = 0; k < NB; ++k)
+            for (int k = 0; k < NB; k += 2)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = mfma32(cat8(fx[h][k], fx[h][k + 1]), cat8(fy[k], fy[k + 1]), acc[h]);
             *reinterpret_cast<half8*>(rec + R::U + ((size_t)(nt * (C / 32) + kk) * 64 + lane) * 16) =
                 cat8(to_h4(acc[0]), to_h4(acc[1]));
         }
         lds_barrier();
+        issue(nx, 2);
         // ---------------- Q̃^T = Qs^T - W^T P^T (fragments of Q̃ out); P's upper tiles are zero
 #pragma unroll
         for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
@@ -541,9 +582,10 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             for (int h = 0; h < 2; ++h) fq[h] = ld_h4(sQ + (16 * rt + r16) * LDE + 32 * kk + 16 * h + g4);
             floatx4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-            for (int k = 0; k < NB; ++k)
+            for (int k = 0; k < NB; k += 2)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) acc[h] = mfma16(fx[h][k], fy[k], acc[h]);
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = mfma32(cat8(fx[h][k], fx[h][k + 1]), cat8(fy[k], fy[k + 1]), acc[h]);
             const half4 q0 = to_h4(f4(fq[0]) - acc[0]), q1 = to_h4(f4(fq[1]) - acc[1]);
             *reinterpret_cast<half8*>(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16) = cat8(q0, q1);
             if constexpr (BL) {
