@@ -87,7 +87,7 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
     gdr::FwdParams p;
     p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
-    p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr;
+    p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
     p.BH = B * H; p.T = T; p.flags = flags;
     if (two_pass) return from_hip(gdr::launch_fwd_wy(p, d_k, d_v, workspace, (hipStream_t)stream));
     int used = 0;
@@ -150,12 +150,17 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
     p.dO = dO; p.dSf = dS_final;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dla = dlog_alpha; p.db = db; p.dw = dw; p.dS0 = dS0;
     p.states = nullptr; p.dstates = nullptr; p.records = nullptr;
+    p.state_frags = nullptr; p.dstate_frags = nullptr;
     p.BH = B * H; p.T = T; p.flags = flags;
     if (need > 0) {
         const size_t sb = gdr::bwd_states_bytes(B * H, T, d_k, d_v, chunk, flags);
         char* base = reinterpret_cast<char*>(workspace);
+        // states, then state gradients (fp32 rows for the generic path, f16
+        // fragments for the two-pass path), then the two-pass forward's records
         p.states = reinterpret_cast<float*>(base);
         p.dstates = reinterpret_cast<float*>(base + sb);
+        p.state_frags = base;
+        p.dstate_frags = base + sb;
         if (need > 2 * sb) p.records = base + 2 * sb;
     }
     return from_hip(gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream));

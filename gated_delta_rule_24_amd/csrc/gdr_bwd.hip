@@ -870,9 +870,16 @@ bool bwd_supported(int dk, int dv, int chunk, uint32_t /*flags*/) {
     return dk == dv && (dk == 64 || dk == 128) && (chunk == 32 || chunk == 64);
 }
 
+// the two-pass path keeps S' and the state gradients as f16 fragments, the
+// generic path as fp32 rows
+static bool bwd_two_pass(int dk, int dv, int T, int cb, uint32_t flags) {
+    return T > 0 && fwd_wy_supported(dk, dv, cb, flags);
+}
+
 size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags) {
     const int cb = bwd::bwd_chunk(chunk, flags);
-    return (size_t)BH * (size_t)(T / cb) * (size_t)dk * (size_t)dv * sizeof(float);
+    const size_t elem = bwd_two_pass(dk, dv, T, cb, flags) ? 2 : sizeof(float);
+    return (size_t)BH * (size_t)(T / cb) * (size_t)dk * (size_t)dv * elem;
 }
 
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags) {
@@ -880,7 +887,7 @@ size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t fl
     // chunk-start states, chunk-end state gradients, and (where the two-pass forward
     // recomputes the states) its per-chunk records
     size_t n = 2 * bwd_states_bytes(BH, T, dk, dv, chunk, flags);
-    if (T > 0 && fwd_wy_supported(dk, dv, cb, flags)) n += fwd_wy_workspace_bytes(BH, T, dk, dv, true);
+    if (bwd_two_pass(dk, dv, T, cb, flags)) n += fwd_wy_workspace_bytes(BH, T, dk, dv, true);
     return n;
 }
 
@@ -898,26 +905,29 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
     // 1. chunk-start states
     FwdParams f;
     f.q = p.q; f.k = p.k; f.v = p.v; f.la = p.la; f.b = p.b; f.w = p.w; f.S0 = p.S0;
-    f.o = nullptr; f.Sf = nullptr; f.states = p.states;
+    f.o = nullptr; f.Sf = nullptr; f.states = nullptr; f.state_frags = nullptr;
     f.BH = p.BH; f.T = p.T; f.flags = p.flags & ~(uint32_t)GDR_OUT_BF16;
     hipError_t e;
-    const bool wyp = p.records && fwd_wy_supported(dk, dv, cb, p.flags);
-    if (wyp) {
-        // two-pass forward (its records keep the operands the reverse chain needs),
-        // then the reverse chain over those records
+    if (bwd_two_pass(dk, dv, p.T, cb, p.flags)) {
+        if (!p.records || !p.state_frags || !p.dstate_frags) return hipErrorInvalidValue;
+        // two-pass forward (its records keep the operands the reverse passes need,
+        // its chain the decayed chunk-start states), the reverse chain over those
+        // records, then every chunk's gradients
+        f.state_frags = p.state_frags;
         e = launch_fwd_wy(f, dk, dv, p.records, st, true);
         if (e != hipSuccess) return e;
         e = launch_bwd_dchain(p, dk, dv, p.records, st);
         if (e != hipSuccess) return e;
-    } else {
-        int used = 0;
-        e = launch_fwd(f, dk, dv, cb, st, &used);
-        if (e != hipSuccess) return e;
-        if (used != cb) return hipErrorInvalidValue;
+        return launch_bwd_wgrad(p, dk, dv, p.records, st);
     }
+    f.states = p.states;
+    int used = 0;
+    e = launch_fwd(f, dk, dv, cb, st, &used);
+    if (e != hipSuccess) return e;
+    if (used != cb) return hipErrorInvalidValue;
     // 2 and 3
     const bool f32 = (p.flags & GDR_ACT_F32) != 0;
-    const bool ds = !wyp;
+    const bool ds = true;
     if (dk == 128) {
         if (f32) return bwd::launch_t<128, 128, 32, true>(p, st, ds);
         return cb == 64 ? bwd::launch_t<128, 128, 64, false>(p, st, ds) : bwd::launch_t<128, 128, 32, false>(p, st, ds);

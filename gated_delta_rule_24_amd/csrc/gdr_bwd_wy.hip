@@ -1,0 +1,782 @@
+// Backward passes over the two-pass forward's records (bf16 activations,
+// chunk 64, d_k = d_v in {64, 128}).
+#include "gdr_device.h"
+#include "gdr_launch.h"
+#include "gdr_wy.h"
+
+namespace gdr {
+
+namespace wy {
+
+// Reverse chain of the backward.  With the forward's chunk operands, the
+// gradient of the chunk-start state follows from the gradient D of the
+// chunk-end state as
+//   diag(e^{g_C}) (D + Q̃^T dO - W^T (Kh D)),
+// because the triangular solve of the reverse mode folds into W and Q̃
+// (E^T T^T = W^T and Qs - P W = Q̃).  One workgroup of two waves per (head,
+// 16-column strip): wave 0 carries D (Z = Kh D, D += F - W^T Z, D *= gamma)
+// and stores every chunk-end gradient; wave 1 computes F = Q̃^T dO one chunk
+// ahead (nothing on the chain depends on it) and publishes it in LDS.  Both
+// prefetch their operands two chunks ahead.
+template <int DK, int NK2>
+struct DFrags {
+    half8 kw[DK / 32][C / 16], wt[DK / 16][NK2];
+    floatx4 gm[DK / 16];
+    int flag;
+};
+template <int DK, int NK2>
+struct FFrags {
+    half8 qt[DK / 16][NK2];
+    uint32_t dob[NK2][8];       // raw bf16 dO values (K = tokens)
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsigned char* ws) {
+    using R = Rec<DK, DV>;
+    constexpr size_t RB = R::bwd_bytes;
+    constexpr int NST = DV / 16, NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
+    __shared__ __align__(16) floatx4 sF[2][NKT][64];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lid / NST, nt = lid % NST;
+    const int NC = p.T / C;
+    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
+    const int n_l = lane & 15, g4 = 4 * (lane >> 4), col = 16 * nt + n_l;
+    auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
+    };
+    auto recp = [&](int c) __attribute__((always_inline)) {
+        return rec0 + (size_t)(c < 0 ? 0 : c) * RB;
+    };
+
+    if (wave == 1) {
+        // ------------------------------------------------ F = Q̃^T dO, one chunk ahead
+        using F = FFrags<DK, NK2>;
+        const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dO);
+        auto fetch = [&](int c, F& f) __attribute__((always_inline)) {
+            const int cc = c < 0 ? 0 : c;
+            const unsigned char* rec = recp(cc);
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int kk = 0; kk < NK2; ++kk) f.qt[mt][kk] = frag(rec, R::QT + (size_t)(mt * NK2 + kk) * 1024);
+            const size_t tok0 = (size_t)bh * p.T + (size_t)cc * C;
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 32 * kk + (j < 4 ? g4 + j : 16 + g4 + j - 4);
+                    f.dob[kk][j] = dO[(tok0 + t) * DV + col];
+                }
+        };
+        auto compute = [&](F& f, int buf) __attribute__((always_inline)) {
+            half8 dof[NK2];
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dof[kk][j] = (_Float16)__uint_as_float(f.dob[kk][j] << 16);
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NK2; ++kk) acc = mfma32(f.qt[mt][kk], dof[kk], acc);
+                sF[buf][mt][lane] = acc;
+            }
+        };
+        F fa, fb;
+        if (NC > 0) {
+            fetch(NC - 1, fa);
+            fetch(NC - 2, fb);
+            compute(fa, 0);
+            fetch(NC - 3, fa);
+        }
+        // iteration j (chunk NC-1-j on wave 0) prepares chunk NC-2-j
+        auto step = [&](int j, F& f) __attribute__((always_inline)) {
+            lds_barrier();
+            const int c = NC - 2 - j;
+            if (c >= 0) {
+                compute(f, (j + 1) & 1);
+                fetch(c - 2, f);
+            }
+        };
+        for (int j = 0; j < NC; j += 2) {
+            step(j, fb);
+            if (j + 1 < NC) step(j + 1, fa);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- wave 0: D, backwards
+    using F = DFrags<DK, NK2>;
+    floatx4 D[NKT];
+#pragma unroll
+    for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            D[mt][i] = p.dSf ? p.dSf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] : 0.f;
+    auto fetch_kg = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) f.kw[kk][rt] = frag(rec, R::KW + (size_t)(rt * NKK + kk) * 1024);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) f.gm[mt] = *reinterpret_cast<const floatx4*>(rec + R::G + (16 * mt + g4) * 4);
+        f.flag = *reinterpret_cast<const int*>(rec + R::G + DK * 4);
+    };
+    auto fetch_w = [&](int c, F& f) __attribute__((always_inline)) {
+        const unsigned char* rec = recp(c);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < NK2; ++kk) f.wt[mt][kk] = frag(rec, R::WT + (size_t)(mt * NK2 + kk) * 1024);
+    };
+    F fa, fb;
+    if (NC > 0) {
+        fetch_kg(NC - 1, fa); fetch_w(NC - 1, fa);
+        fetch_kg(NC - 2, fb); fetch_w(NC - 2, fb);
+    }
+    bool poisoned = false;
+    const float qnan = __builtin_nanf("");
+    half8 nan8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nan8[e] = (_Float16)qnan;
+    auto step = [&](int j, F& f) __attribute__((always_inline)) {
+        const int c = NC - 1 - j;
+        // Z = Kh D; the f16 fragments of D are also the gradient kernel's copy of
+        // this chunk's end-state gradient
+        half8 df[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) df[kk] = cat8(to_h4(D[2 * kk]), to_h4(D[2 * kk + 1]));
+        {
+            using SFB = StateFrag<DK, DV>;
+            unsigned char* dst = reinterpret_cast<unsigned char*>(p.dstate_frags) + ((size_t)bh * NC + c) * SFB::bytes;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                *reinterpret_cast<half8*>(dst + SFB::block(nt, kk) + (size_t)lane * 16) = poisoned ? nan8 : df[kk];
+        }
+        if (f.flag) poisoned = true;
+        floatx4 Z[NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Z[rt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) Z[rt] = mfma32(f.kw[kk][rt], df[kk], Z[rt]);
+        lds_barrier();                                   // F of chunk c is published
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) D[mt] += sF[j & 1][mt][lane];
+        // D += -W^T Z, then D = diag(gamma) D
+        half8 zf[NK2];
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) zf[kk] = cat8(to_h4(-Z[2 * kk]), to_h4(-Z[2 * kk + 1]));
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt) D[mt] = mfma32(f.wt[mt][kk], zf[kk], D[mt]);
+        const floatx4* gm = f.gm;
+        floatx4 g2[NKT];
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) g2[mt] = gm[mt];
+        fetch_kg(c - 2, f);
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt) D[mt] = D[mt] * g2[mt];
+        fetch_w(c - 2, f);
+    };
+    for (int j = 0; j < NC; j += 2) {
+        step(j, fa);
+        if (j + 1 < NC) step(j + 1, fb);
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.dS0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] = poisoned ? qnan : D[mt][i];
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t st) {
+    hipLaunchKernelGGL((dchain_kernel<DK, DV>), dim3((unsigned)(p.BH * (DV / 16))), dim3(128), 0, st, p,
+                       reinterpret_cast<const unsigned char*>(ws));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients
+// ---------------------------------------------------------------------------
+// One workgroup of four waves per chunk, all chunks in parallel.  Inputs: the
+// chunk's record, its decayed start state S' and its end-state gradient D (f16
+// fragments), dO and the activations.  With U = Ũ - W S', dU = Kh D + P^T dO and
+// dR = T^T dU (the reverse of the triangular solve):
+//   dP  = lower(dO U^T),        dA  = strict_lower(-dR U^T),
+//   dQs = dO S'^T + dP Kh,       dE  = -dR S'^T + dA Kh,
+//   dKh = U D^T + dA^T E + dP^T Qs,
+// and the log-decay gradient dlog_alpha_t = Phi - sum_{r<t} dg_r with
+// dg = dE ⊙ E + dQs ⊙ Qs - dKh ⊙ Kh and, per channel,
+//   Phi = rowsum(dS' ⊙ S'),  dS' = D + Qs^T dO - E^T dR,
+// computed as rowsum(D ⊙ S') + colsum(Qs ⊙ dO S'^T) - colsum(E ⊙ dR S'^T), so
+// that dS' itself is never formed.
+// Phase A splits the value columns over the waves: U, dU, dR, and from dR the
+// value-side gradients dv = dR ⊙ w, dw = dR ⊙ v.  U, dR and dO go to LDS with
+// tokens as rows.  Phase B splits the channels: the value reductions
+// S' dO^T, S' dR^T and D U^T (channel x token accumulators), Phi, and the
+// small dP and dA.  Phase C adds the token reductions and forms the
+// element-wise gradients of q, k, b and log alpha in the same channel split.
+// Register tiles change orientation on the MFMA unit (product with the
+// identity), so no operand is gathered from LDS with strided scalar reads.
+template <int D>
+struct WgradLayout {
+    static constexpr int LDX = D + 8;      // U, dR, dO: [C][LDX] f16, rows = tokens
+    static constexpr int LDP = C + 8;      // dP, dA, their transposes: [C][LDP] f16
+    static constexpr size_t oU = 0;
+    static constexpr size_t oR = oU + (size_t)C * LDX * 2;
+    static constexpr size_t oO = oR + (size_t)C * LDX * 2;
+    static constexpr size_t endB = oO + (size_t)C * LDX * 2;
+    static constexpr size_t oP = 0;                               // after phase B
+    static constexpr size_t oA = oP + (size_t)C * LDP * 2;
+    static constexpr size_t oPT = oA + (size_t)C * LDP * 2;
+    static constexpr size_t oAT = oPT + (size_t)C * LDP * 2;
+    static constexpr size_t endC = oAT + (size_t)C * LDP * 2;
+    static constexpr int NW = D / 16;      // waves: one 16-column value tile (phase A) and
+                                           // one 16-channel tile (phases B, C) each
+    static constexpr size_t oRed = endB > endC ? endB : endC;     // [3][NW][C] fp32
+    static constexpr size_t oPhi = oRed + (size_t)3 * NW * C * 4; // [NW] fp32
+    static constexpr size_t bytes = oPhi + (size_t)NW * 4;
+};
+
+__device__ __forceinline__ half4 bf16x4_to_h4(uint2 u) {
+    half4 h;
+    h[0] = (_Float16)__uint_as_float(u.x << 16);
+    h[1] = (_Float16)__uint_as_float(u.x & 0xffff0000u);
+    h[2] = (_Float16)__uint_as_float(u.y << 16);
+    h[3] = (_Float16)__uint_as_float(u.y & 0xffff0000u);
+    return h;
+}
+__device__ __forceinline__ float hsum4(floatx4 v) { return (v[0] + v[1]) + (v[2] + v[3]); }
+__device__ __forceinline__ floatx4 splat4(float x) {
+    floatx4 f;
+    f[0] = f[1] = f[2] = f[3] = x;
+    return f;
+}
+__device__ __forceinline__ floatx4 shfl4(floatx4 v, int src, int width) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __shfl(v[i], src, width);
+    return r;
+}
+// inclusive prefix sum over the 16 lanes of each lane group (lane & 15 order)
+__device__ __forceinline__ floatx4 scan16(floatx4 x, int r16) {
+#pragma unroll
+    for (int d = 1; d < 16; d *= 2) {
+        floatx4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = __shfl_up(x[i], d, 16);
+        if (r16 >= d) x += y;
+    }
+    return x;
+}
+__device__ __forceinline__ floatx4 expv4(floatx4 x) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __expf(x[i]);
+    return r;
+}
+
+// g - g_C for the four channels 4g..4g+3 of a 16-channel tile (or the scalar
+// decay) at tokens 16 tt + r, tt < 4: the in-chunk prefix of log alpha over the
+// lanes of each group and across the four token tiles
+template <int D, bool AS>
+__device__ __forceinline__ void chunk_decay(const float* lag, int ch0, int r16, floatx4 (&gm)[4]) {
+    floatx4 carry = zero4();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + r16;
+        const floatx4 la = AS ? splat4(lag[t]) : *reinterpret_cast<const floatx4*>(lag + t * D + ch0);
+        const floatx4 x = scan16(la, r16);
+        gm[tt] = x + carry;
+        carry += shfl4(x, 15, 16);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) gm[tt] -= carry;
+}
+
+template <int D, bool AS, bool BS, bool WS>
+__global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsigned char* ws) {
+    using R = Rec<D, D>;
+    using SFB = StateFrag<D, D>;
+    using L = WgradLayout<D>;
+    constexpr size_t RB = R::bwd_bytes;
+    constexpr int NW = L::NW, TPW = 1, NKK = D / 32, NB = C / 16, NK2 = C / 32;
+    constexpr int LDX = L::LDX, LDP = L::LDP;
+    static_assert(NW * 16 == D && L::bytes <= 64 * 1024, "layout");
+    __shared__ __align__(16) unsigned char smem[L::bytes];
+    _Float16* sU = reinterpret_cast<_Float16*>(smem + L::oU);
+    _Float16* sR = reinterpret_cast<_Float16*>(smem + L::oR);
+    _Float16* sO = reinterpret_cast<_Float16*>(smem + L::oO);
+    _Float16* sP = reinterpret_cast<_Float16*>(smem + L::oP);
+    _Float16* sA = reinterpret_cast<_Float16*>(smem + L::oA);
+    _Float16* sPT = reinterpret_cast<_Float16*>(smem + L::oPT);
+    _Float16* sAT = reinterpret_cast<_Float16*>(smem + L::oAT);
+    float* sRed = reinterpret_cast<float*>(smem + L::oRed);
+    float* sPhi = reinterpret_cast<float*>(smem + L::oPhi);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+    const int NC = p.T / C;
+    const int bh = (int)blockIdx.x / NC, c = (int)blockIdx.x % NC;
+    const size_t chunk = (size_t)bh * NC + c;
+    const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+    const unsigned char* rec = ws + chunk * RB;
+    const unsigned char* sfr = reinterpret_cast<const unsigned char*>(p.state_frags) + chunk * SFB::bytes;
+    const unsigned char* dfr = reinterpret_cast<const unsigned char*>(p.dstate_frags) + chunk * SFB::bytes;
+    // chunk bases (uniform) and 32-bit lane offsets keep the addresses in scalar registers
+    const size_t ea = tok0 * D;                                  // element offset, [T][D] tensors
+    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + ea;
+    const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + ea;
+    const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b) + (BS ? tok0 : ea);
+    const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + ea;
+    const uint16_t* wg = reinterpret_cast<const uint16_t*>(p.w) + (WS ? tok0 : ea);
+    const uint16_t* og = reinterpret_cast<const uint16_t*>(p.dO) + ea;
+    const float* lag = p.la + (AS ? tok0 : ea);
+    float* dqg = p.dq + ea;
+    float* dkg = p.dk + ea;
+    float* dvg = p.dv + ea;
+    float* dbg = p.db + (BS ? tok0 : ea);
+    float* dwg = p.dw + (WS ? tok0 : ea);
+    float* dlag = p.dla + (AS ? tok0 : ea);
+    const half4 id = ident4(lane);
+    const int lo16 = lane * 16;
+    auto frag = [&](const unsigned char* base, size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(base + off + lo16);
+    };
+    const float poison = *reinterpret_cast<const int*>(rec + R::G + D * 4) ? __builtin_nanf("") : 0.f;
+
+    // ================= phase A: value columns 16 (TPW wave + j) .. +15, all tokens
+    floatx4 Y[TPW][NB], Z[TPW][NB];      // W S' and Kh D (+ P^T dO)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Y[j][rt] = Z[j][rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        half8 fw[NB], fk[NB], fs[TPW], fd[TPW];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            fw[rt] = frag(rec, R::W + (size_t)(rt * NKK + kk) * 1024);
+            fk[rt] = frag(rec, R::KW + (size_t)(rt * NKK + kk) * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            fs[j] = frag(sfr, SFB::block(TPW * wave + j, kk));
+            fd[j] = frag(dfr, SFB::block(TPW * wave + j, kk));
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+                Y[j][rt] = mfma32(fw[rt], fs[j], Y[j][rt]);
+                Z[j][rt] = mfma32(fk[rt], fd[j], Z[j][rt]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // dO: rows to LDS, and columns (K = tokens) for P^T dO
+    half8 dov[TPW][NK2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int vt = TPW * wave + j;
+        floatx4 tq[NB];
+#pragma unroll
+        for (int st = 0; st < NB; ++st) {
+            const int ix = (16 * st + r16) * D + 16 * vt + g4;
+            const half4 h = bf16x4_to_h4(*reinterpret_cast<const uint2*>(og + ix));
+            *reinterpret_cast<half4*>(sO + (16 * st + r16) * LDX + 16 * vt + g4) = h;
+            tq[st] = swap16(h, id);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) dov[j][kk] = cat8(to_h4(tq[2 * kk]), to_h4(tq[2 * kk + 1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dU = Kh D + P^T dO  (P^T blocks left of the diagonal pair are zero)
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int kk = rt / 2; kk < NK2; ++kk) {
+            const half8 fpt = frag(rec, R::PT + (size_t)(rt * NK2 + kk) * 1024);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) Z[j][rt] = mfma32(fpt, dov[j][kk], Z[j][rt]);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    // dR = T^T dU
+    half8 duf[TPW][NK2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) duf[j][kk] = cat8(to_h4(Z[j][2 * kk]), to_h4(Z[j][2 * kk + 1]));
+    floatx4 dR[TPW][NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) dR[j][rt] = zero4();
+#pragma unroll
+        for (int kk = rt / 2; kk < NK2; ++kk) {
+            const half8 ftt = frag(rec, R::TT + (size_t)(rt * NK2 + kk) * 1024);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) dR[j][rt] = mfma32(ftt, duf[j][kk], dR[j][rt]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // U = Ũ - W S'  -> LDS rows (tokens)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int vt = TPW * wave + j;
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) {
+            const half8 ur = frag(rec, R::U + (size_t)(vt * NK2 + kk) * 1024);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rt = 2 * kk + h;
+                const floatx4 u = f4(h ? hi4(ur) : lo4(ur)) - Y[j][rt];
+                const floatx4 ut = swap16(to_h4(u), id);
+                *reinterpret_cast<half4*>(sU + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(ut);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dR -> LDS rows; dv = dR ⊙ w and dw = dR ⊙ v from the row layout (fp32:
+    // the transposed f16 value plus the transposed f16 remainder)
+    float dwp[NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) dwp[rt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int vt = TPW * wave + j;
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            const half4 hi = to_h4(dR[j][rt]);
+            const floatx4 t1 = swap16(hi, id);
+            *reinterpret_cast<half4*>(sR + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(t1);
+            const floatx4 x = mfma16(to_h4(dR[j][rt] - f4(hi)), id, t1);
+            const int t = 16 * rt + r16, ix = t * D + 16 * vt + g4;
+            const floatx4 v4 = load_act4<false>(vg, ix);
+            const floatx4 w4 = WS ? splat4(bf16_to_f32(wg[t])) : load_act4<false>(wg, ix);
+            *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
+            if constexpr (WS) dwp[rt] += hsum4(x * v4);
+            else *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
+        }
+    }
+    if constexpr (WS) {
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            float v = dwp[rt];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (g4 == 0) sRed[(0 * NW + wave) * C + 16 * rt + r16] = v;
+        }
+    }
+    lds_barrier();
+
+    // ================= phase B: channels 16 (TPW wave + j) .. +15, all tokens
+    // Per 32-column step kv: S' and D with K = value columns (rows of the state,
+    // from the column fragments by the identity product), rowsum(D ⊙ S'), and
+    // A1 = S' dO^T, A2 = S' dR^T, A3 = D U^T  (rows = channels, columns = tokens)
+    floatx4 A1[TPW][NB], A2[TPW][NB], A3[TPW][NB];
+    float phd[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        phd[j] = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt) A1[j][tt] = A2[j][tt] = A3[j][tt] = zero4();
+    }
+#pragma unroll
+    for (int kv = 0; kv < NKK; ++kv) {
+        half8 sc[TPW], dc[TPW];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int ct = TPW * wave + j, kk = ct >> 1, h = ct & 1;
+            floatx4 xs[2], xd[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const half8 fs = frag(sfr, SFB::block(2 * kv + e, kk));
+                const half8 fd = frag(dfr, SFB::block(2 * kv + e, kk));
+                xs[e] = swap16(h ? hi4(fs) : lo4(fs), id);    // S'[16ct + r][32kv + 16e + 4g + i]
+                xd[e] = swap16(h ? hi4(fd) : lo4(fd), id);
+                phd[j] += hsum4(xs[e] * xd[e]);
+            }
+            sc[j] = cat8(to_h4(xs[0]), to_h4(xs[1]));
+            dc[j] = cat8(to_h4(xd[0]), to_h4(xd[1]));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt) {
+            const int off = (16 * tt + r16) * LDX + 32 * kv + g4;
+            const half8 bo = cat8(ld_h4(sO + off), ld_h4(sO + off + 16));
+            const half8 br = cat8(ld_h4(sR + off), ld_h4(sR + off + 16));
+            const half8 bu = cat8(ld_h4(sU + off), ld_h4(sU + off + 16));
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                A1[j][tt] = mfma32(sc[j], bo, A1[j][tt]);
+                A2[j][tt] = mfma32(sc[j], br, A2[j][tt]);
+                A3[j][tt] = mfma32(dc[j], bu, A3[j][tt]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // dP^T and dA^T tiles (s-tile st <= t-tile tt): Res[s][t] = sum_v U[s][v] X[t][v]
+    // with X = dO (dP) or dR (-dA); twenty tiles over the waves
+    constexpr int NPA = 2 * NB * (NB + 1) / 2, PAW = (NPA + NW - 1) / NW;
+    floatx4 pa[PAW];
+#pragma unroll
+    for (int m = 0; m < PAW; ++m) {
+        const int it = wave + NW * m, kind = it / (NPA / 2);
+        pa[m] = zero4();
+        if (it >= NPA) break;
+        int t = it % (NPA / 2), tt = 0;
+        while (t > tt) { t -= tt + 1; ++tt; }
+        const int st = t;
+        const _Float16* xs = kind ? sR : sO;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kv = 0; kv < NKK; ++kv) {
+            const int ou = (16 * st + r16) * LDX + 32 * kv + g4, ox = (16 * tt + r16) * LDX + 32 * kv + g4;
+            acc = mfma32(cat8(ld_h4(sU + ou), ld_h4(sU + ou + 16)), cat8(ld_h4(xs + ox), ld_h4(xs + ox + 16)), acc);
+        }
+        pa[m] = acc;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();          // U, dR, dO are no longer read: their space takes dP and dA
+
+    // dP, dA (rows = t) and their transposes (rows = s); strict/inclusive masks on
+    // the diagonal tiles; tiles beyond the diagonal are zero
+#pragma unroll
+    for (int m = 0; m < PAW; ++m) {
+        const int it = wave + NW * m, kind = it / (NPA / 2);
+        if (it >= NPA) break;
+        int t = it % (NPA / 2), tt = 0;
+        while (t > tt) { t -= tt + 1; ++tt; }
+        const int st = t;
+        floatx4 v = pa[m];
+        if (st == tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool keep = kind ? (g4 + i < r16) : (g4 + i <= r16);
+                v[i] = keep ? v[i] : 0.f;
+            }
+        }
+        const half4 hv = to_h4(v);
+        _Float16* rows = kind ? sA : sP;
+        _Float16* cols = kind ? sAT : sPT;
+        *reinterpret_cast<half4*>(rows + (16 * tt + r16) * LDP + 16 * st + g4) = hv;
+        *reinterpret_cast<half4*>(cols + (16 * st + r16) * LDP + 16 * tt + g4) = to_h4(swap16(hv, id));
+    }
+    {
+        const half4 z4 = to_h4(zero4());
+        for (int idx = tid; idx < 6 * 16 * 4 * 4; idx += 64 * NW) {
+            const int mtx = idx & 3, q = (idx >> 2) & 3, row = (idx >> 4) & 15, pr = idx >> 8;
+            const int a = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+            const int b = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+            _Float16* base = mtx == 0 ? sP : mtx == 1 ? sA : mtx == 2 ? sPT : sAT;
+            const int rt = mtx < 2 ? a : b, cb = mtx < 2 ? b : a;
+            *reinterpret_cast<half4*>(base + (16 * rt + row) * LDP + 16 * cb + 4 * q) = z4;
+        }
+    }
+    // element-wise part: g - g_C (in-chunk prefix over tokens), E, Qs, Phi, and the
+    // channel-row fragments of E and Qs (K = tokens) for the token reductions
+    floatx4 phi[TPW];
+    half8 ef[TPW][NK2], qf[TPW][NK2], kf[TPW][NK2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int ct = TPW * wave + j;
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) kf[j][kk] = frag(rec, R::K + (size_t)(ct * NK2 + kk) * 1024);
+        floatx4 gm[NB];
+        chunk_decay<D, AS>(lag, 16 * ct + g4, r16, gm);
+        floatx4 p2 = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) {
+            floatx4 eT[2], qT[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tt = 2 * kk + h;
+                const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
+                const floatx4 eg = expv4(gm[tt]);
+                const floatx4 q4 = load_act4<false>(qg, ix), k4 = load_act4<false>(kg, ix);
+                const floatx4 b4 = BS ? splat4(bf16_to_f32(bg[t])) : load_act4<false>(bg, ix);
+                const floatx4 E = b4 * k4 * eg, Qs = q4 * eg;
+                p2 += Qs * A1[j][tt] - E * A2[j][tt];
+                eT[h] = swap16(to_h4(-E), id);     // -E: the dA tiles hold -dA
+                qT[h] = swap16(to_h4(Qs), id);
+            }
+            ef[j][kk] = cat8(to_h4(eT[0]), to_h4(eT[1]));
+            qf[j][kk] = cat8(to_h4(qT[0]), to_h4(qT[1]));
+        }
+        // Phi: the token sum over the 16 lanes of a group, plus rowsum(D ⊙ S')
+        // (held per channel r by all four lane groups after the reduction)
+#pragma unroll
+        for (int d = 1; d < 16; d *= 2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p2[i] += __shfl_xor(p2[i], d, 64);
+        float pd = phd[j];
+        pd += __shfl_xor(pd, 16, 64);
+        pd += __shfl_xor(pd, 32, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) phi[j][i] = p2[i] + __shfl(pd, g4 + i, 64);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+
+    // ================= phase C: token reductions
+    //   A1 += Kh^T-rows dP,   A2 += Kh^T-rows (-dA)   (so dE = -A2),
+    //   A3 += (-E) (-dA)^T + Qs dP^T   (dKh)
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+        const int row = (16 * tt + r16) * LDP + g4;
+#pragma unroll
+        for (int kk = 0; kk < NK2; ++kk) {
+            if (2 * kk <= tt) {
+                const half8 bp = cat8(ld_h4(sP + row + 32 * kk), ld_h4(sP + row + 32 * kk + 16));
+                const half8 ba = cat8(ld_h4(sA + row + 32 * kk), ld_h4(sA + row + 32 * kk + 16));
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    A1[j][tt] = mfma32(kf[j][kk], bp, A1[j][tt]);
+                    A2[j][tt] = mfma32(kf[j][kk], ba, A2[j][tt]);
+                }
+            }
+            if (2 * kk + 1 >= tt) {
+                const half8 bpt = cat8(ld_h4(sPT + row + 32 * kk), ld_h4(sPT + row + 32 * kk + 16));
+                const half8 bat = cat8(ld_h4(sAT + row + 32 * kk), ld_h4(sAT + row + 32 * kk + 16));
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    A3[j][tt] = mfma32(ef[j][kk], bat, A3[j][tt]);
+                    A3[j][tt] = mfma32(qf[j][kk], bpt, A3[j][tt]);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // element-wise gradients; lane (r, g): token 16 tt + r, channels 16 ct + 4g .. +3
+    float dbs[NB], dgs[NB], phs = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) dbs[tt] = dgs[tt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int ct = TPW * wave + j;
+        floatx4 carry = zero4();
+        phs += hsum4(phi[j]);
+        floatx4 gm[NB];
+        chunk_decay<D, AS>(lag, 16 * ct + g4, r16, gm);
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt) {
+            const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
+            const floatx4 eg = expv4(gm[tt]), ek = expv4(-gm[tt]);
+            const floatx4 q4 = load_act4<false>(qg, ix), k4 = load_act4<false>(kg, ix);
+            const floatx4 b4 = BS ? splat4(bf16_to_f32(bg[t])) : load_act4<false>(bg, ix);
+            const floatx4 dQs = A1[j][tt], dE = -A2[j][tt], dKh = A3[j][tt];
+            *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
+            *reinterpret_cast<floatx4*>(dkg + ix) = dE * b4 * eg + dKh * ek + poison;
+            const floatx4 dbv = dE * k4 * eg;
+            if constexpr (BS) dbs[tt] += hsum4(dbv);
+            else *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
+            const floatx4 dg = dE * (b4 * k4 * eg) + dQs * (q4 * eg) - dKh * (k4 * ek);
+            if constexpr (AS) {
+                dgs[tt] += hsum4(dg);
+            } else {
+                const floatx4 incl = scan16(dg, r16);
+                *reinterpret_cast<floatx4*>(dlag + ix) = phi[j] - (carry + (incl - dg)) + poison;
+                carry += shfl4(incl, 15, 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (AS || BS) {
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt) {
+            float vb = dbs[tt], vg2 = dgs[tt];
+            vb += __shfl_xor(vb, 16, 64);
+            vb += __shfl_xor(vb, 32, 64);
+            vg2 += __shfl_xor(vg2, 16, 64);
+            vg2 += __shfl_xor(vg2, 32, 64);
+            if (g4 == 0) {
+                sRed[(1 * NW + wave) * C + 16 * tt + r16] = vb;
+                sRed[(2 * NW + wave) * C + 16 * tt + r16] = vg2;
+            }
+        }
+        // Phi summed over this wave's channels (each lane group holds the same sums)
+        if constexpr (AS) {
+            float v = phs;
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (lane == 0) sPhi[wave] = v;
+        }
+    }
+    if constexpr (AS || BS || WS) {
+        lds_barrier();
+        if (wave == 0) {
+            const int t = lane;      // C == 64 tokens, one per lane
+            auto wsum = [&](int which) __attribute__((always_inline)) {
+                float a = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) a += sRed[(which * NW + w) * C + t];
+                return a;
+            };
+            if constexpr (WS) dwg[t] = wsum(0) + poison;
+            if constexpr (BS) dbg[t] = wsum(1) + poison;
+            if constexpr (AS) {
+                const float dg = wsum(2);
+                float incl = dg;
+#pragma unroll
+                for (int d = 1; d < 64; d *= 2) {
+                    const float u = __shfl_up(incl, d, 64);
+                    if (t >= d) incl += u;
+                }
+                float ptot = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) ptot += sPhi[w];
+                dlag[t] = ptot - (incl - dg) + poison;
+            }
+        }
+    }
+}
+
+template <int D, bool AS, bool BS, bool WS>
+static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t st) {
+    const int NC = p.T / C;
+    hipLaunchKernelGGL((wgrad_kernel<D, AS, BS, WS>), dim3((unsigned)(p.BH * NC)), dim3(D * 4), 0, st, p,
+                       reinterpret_cast<const unsigned char*>(ws));
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_wgrad(const BwdParams& p, const void* ws, hipStream_t st) {
+    const int m = ((p.flags & GDR_ALPHA_SCALAR) ? 4 : 0) | ((p.flags & GDR_B_SCALAR) ? 2 : 0) |
+                  ((p.flags & GDR_W_SCALAR) ? 1 : 0);
+    switch (m) {
+        case 0: return launch_wgrad_t<D, false, false, false>(p, ws, st);
+        case 1: return launch_wgrad_t<D, false, false, true>(p, ws, st);
+        case 2: return launch_wgrad_t<D, false, true, false>(p, ws, st);
+        case 3: return launch_wgrad_t<D, false, true, true>(p, ws, st);
+        case 4: return launch_wgrad_t<D, true, false, false>(p, ws, st);
+        case 5: return launch_wgrad_t<D, true, false, true>(p, ws, st);
+        case 6: return launch_wgrad_t<D, true, true, false>(p, ws, st);
+        default: return launch_wgrad_t<D, true, true, true>(p, ws, st);
+    }
+}
+
+}  // namespace wy
+
+hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st) {
+    if (dk == 128 && dv == 128) return wy::launch_dchain<128, 128>(p, records, st);
+    if (dk == 64 && dv == 64) return wy::launch_dchain<64, 64>(p, records, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_wgrad(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st) {
+    if (dk == 128 && dv == 128) return wy::launch_wgrad<128>(p, records, st);
+    if (dk == 64 && dv == 64) return wy::launch_wgrad<64>(p, records, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -23,100 +23,11 @@
 // are touched so they are already in L2.  Every fragment feeds both strips.
 #include "gdr_device.h"
 #include "gdr_launch.h"
+#include "gdr_wy.h"
 
 namespace gdr {
 
 namespace wy {
-
-constexpr int C = 64;
-constexpr int NT = 256;
-constexpr float kDecayLimit = 10.0f;    // f16 operand range, as in the other kernels
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Per-chunk record in the workspace (bytes).  The WY pass writes records with
-// non-temporal stores (streamed to memory rather than allocated in L2); that
-// takes the chain pass from about 174 to 162 us on the 2 x 16 x 8192 workload.
-// Fragment blocks are 64 lanes x 16 bytes; lane l = r + 16 g (r = l & 15,
-// g = l >> 4) holds, for a 32-wide K step kk, the K positions 32kk + 4g .. +3
-// followed by 32kk + 16 + 4g .. +3.
-//   W, Q̃  block (rt, kk): row t = 16 rt + r of W (Q̃), K = channels
-//   Kh^T   block (mt, kk): channel 16 mt + r of Kh^T, K = tokens
-//   P      block (rt, kk): row 16 rt + r of P, K = tokens
-//   Ũ      strip nt, block kk: column 16 nt + r of Ũ, K = tokens
-//   G      e^{g_C} per channel (fp32), then an int flag (decay out of range)
-template <int DK, int DV>
-struct Rec {
-    static constexpr size_t W = 0;
-    static constexpr size_t Q = W + (size_t)C * DK * 2;
-    static constexpr size_t K = Q + (size_t)C * DK * 2;
-    static constexpr size_t P = K + (size_t)DK * C * 2;
-    static constexpr size_t U = P + (size_t)C * C * 2;
-    static constexpr size_t G = U + (size_t)C * DV * 2;
-    static constexpr size_t bytes = G + (((size_t)DK * 4 + 16 + 255) & ~size_t(255));
-    static constexpr size_t strip = (size_t)C * 16 * 2;   // Ũ bytes per 16-column strip
-    // appended when the backward consumes the records:
-    //   KW  block (rt, kk): row t = 16 rt + r of Kh, K = channels
-    //   WT  block (mt, kk): channel 16 mt + r of W^T, K = tokens
-    //   QT  block (mt, kk): channel 16 mt + r of Q̃^T, K = tokens
-    static constexpr size_t KW = bytes;
-    static constexpr size_t WT = KW + (size_t)C * DK * 2;
-    static constexpr size_t QT = WT + (size_t)C * DK * 2;
-    static constexpr size_t bwd_bytes = QT + (size_t)C * DK * 2;
-};
-
-// a 16-byte record store, streamed to memory (non-temporal)
-template <typename V>
-__device__ __forceinline__ void st_nt(unsigned char* p, V v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-}
-__device__ __forceinline__ half4 to_h4(floatx4 v) {
-    half4 h;
-    h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
-    return h;
-}
-__device__ __forceinline__ half8 cat8(half4 a, half4 b) {
-    half8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return r;
-}
-__device__ __forceinline__ half4 lo4(half8 v) {
-    half4 r;
-    r[0] = v[0]; r[1] = v[1]; r[2] = v[2]; r[3] = v[3];
-    return r;
-}
-__device__ __forceinline__ half4 hi4(half8 v) {
-    half4 r;
-    r[0] = v[4]; r[1] = v[5]; r[2] = v[6]; r[3] = v[7];
-    return r;
-}
-__device__ __forceinline__ floatx4 f4(half4 h) {
-    floatx4 v;
-    v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
-    return v;
-}
-__device__ __forceinline__ floatx4 mfma16(half4 a, half4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma32(half8 a, half8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
-__device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
-// four halves from a 4-byte aligned address, as two 4-byte reads
-__device__ __forceinline__ half4 ld_h4w(const _Float16* p) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 a = *reinterpret_cast<const h2*>(p), b = *reinterpret_cast<const h2*>(p + 2);
-    half4 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-    return r;
-}
-// four K values of a column (stride ld)
-__device__ __forceinline__ half4 ld_col4(const _Float16* p, int ld) {
-    half4 h;
-    h[0] = p[0]; h[1] = p[ld]; h[2] = p[2 * ld]; h[3] = p[3 * ld];
-    return h;
-}
 
 // ---------------------------------------------------------------------------
 // pass 1: chunk-local WY operands
@@ -620,6 +531,17 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 st_nt(rec + R::WT + ((size_t)(mt * (C / 32) + kk) * 64 + lane) * 16,
                     cat8(ld_h4(src), ld_h4(src + 16)));
             }
+            // P^T and T^T by rows (columns of P and T), K = tokens; blocks left of
+            // the diagonal pair (kk < rt / 2) are zero
+            for (int task = wave; task < NB * (C / 32); task += NT / 64) {
+                const int rt = task / (C / 32), kk = task % (C / 32);
+                if (kk < rt / 2) continue;
+                const size_t off = ((size_t)(rt * (C / 32) + kk) * 64 + lane) * 16;
+                const _Float16* sp = sP + (32 * kk + g4) * LDT + 16 * rt + r16;
+                const _Float16* stt = sT + (32 * kk + g4) * LDT + 16 * rt + r16;
+                st_nt(rec + R::PT + off, cat8(ld_col4(sp, LDT), ld_col4(sp + 16 * LDT, LDT)));
+                st_nt(rec + R::TT + off, cat8(ld_col4(stt, LDT), ld_col4(stt + 16 * LDT, LDT)));
+            }
             lds_barrier();
             for (int task = wave; task < (DK / 16) * (C / 32); task += NT / 64) {
                 const int mt = task / (C / 32), kk = task % (C / 32);
@@ -828,16 +750,7 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     }
     bool poisoned = false;
     auto step = [&](int c, F& f) __attribute__((always_inline)) {
-        if (p.states) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        p.states[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] =
-                            poisoned ? __builtin_nanf("") : S[s][mt][i];
-        }
+        const bool was_poisoned = poisoned;
         if (f.flag) poisoned = true;
         // S' = diag(gamma) S and its f16 fragments (K = channels), published for the output wave
         half8 sf[NS][NKK];
@@ -852,6 +765,20 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
                 sf[s][kk] = cat8(to_h4(S[s][2 * kk]), to_h4(S[s][2 * kk + 1]));
                 sSF[c & 1][s][kk][lane] = sf[s][kk];
             }
+        if (p.state_frags) {
+            // the backward's copy of S' (after an out-of-range chunk: NaN)
+            using SFB = StateFrag<DK, DV>;
+            unsigned char* dst = reinterpret_cast<unsigned char*>(p.state_frags) + ((size_t)bh * NC + c) * SFB::bytes;
+            half8 nan8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nan8[e] = (_Float16)__builtin_nanf("");
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+                    *reinterpret_cast<half8*>(dst + SFB::block(NS * ng + s, kk) + (size_t)lane * 16) =
+                        was_poisoned ? nan8 : sf[s][kk];
+        }
         fetch_g(c + 2, f);
         lds_barrier();
         // Y = W S'
@@ -899,197 +826,6 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
                     p.Sf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + 16 * (NS * ng + s) + n_l] =
                         poisoned ? __builtin_nanf("") : S[s][mt][i];
     }
-}
-
-// Reverse chain of the backward.  With the forward's chunk operands, the
-// gradient of the chunk-start state follows from the gradient D of the
-// chunk-end state as
-//   diag(e^{g_C}) (D + Q̃^T dO - W^T (Kh D)),
-// because the triangular solve of the reverse mode folds into W and Q̃
-// (E^T T^T = W^T and Qs - P W = Q̃).  One workgroup of two waves per (head,
-// 16-column strip): wave 0 carries D (Z = Kh D, D += F - W^T Z, D *= gamma)
-// and stores every chunk-end gradient; wave 1 computes F = Q̃^T dO one chunk
-// ahead (nothing on the chain depends on it) and publishes it in LDS.  Both
-// prefetch their operands two chunks ahead.
-template <int DK, int NK2>
-struct DFrags {
-    half8 kw[DK / 32][C / 16], wt[DK / 16][NK2];
-    floatx4 gm[DK / 16];
-    int flag;
-};
-template <int DK, int NK2>
-struct FFrags {
-    half8 qt[DK / 16][NK2];
-    uint32_t dob[NK2][8];       // raw bf16 dO values (K = tokens)
-};
-
-template <int DK, int DV>
-__global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsigned char* ws) {
-    using R = Rec<DK, DV>;
-    constexpr size_t RB = R::bwd_bytes;
-    constexpr int NST = DV / 16, NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
-    __shared__ __align__(16) floatx4 sF[2][NKT][64];
-
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = lid / NST, nt = lid % NST;
-    const int NC = p.T / C;
-    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
-    const int n_l = lane & 15, g4 = 4 * (lane >> 4), col = 16 * nt + n_l;
-    auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
-        return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
-    };
-    auto recp = [&](int c) __attribute__((always_inline)) {
-        return rec0 + (size_t)(c < 0 ? 0 : c) * RB;
-    };
-
-    if (wave == 1) {
-        // ------------------------------------------------ F = Q̃^T dO, one chunk ahead
-        using F = FFrags<DK, NK2>;
-        const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dO);
-        auto fetch = [&](int c, F& f) __attribute__((always_inline)) {
-            const int cc = c < 0 ? 0 : c;
-            const unsigned char* rec = recp(cc);
-#pragma unroll
-            for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-                for (int kk = 0; kk < NK2; ++kk) f.qt[mt][kk] = frag(rec, R::QT + (size_t)(mt * NK2 + kk) * 1024);
-            const size_t tok0 = (size_t)bh * p.T + (size_t)cc * C;
-#pragma unroll
-            for (int kk = 0; kk < NK2; ++kk)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int t = 32 * kk + (j < 4 ? g4 + j : 16 + g4 + j - 4);
-                    f.dob[kk][j] = dO[(tok0 + t) * DV + col];
-                }
-        };
-        auto compute = [&](F& f, int buf) __attribute__((always_inline)) {
-            half8 dof[NK2];
-#pragma unroll
-            for (int kk = 0; kk < NK2; ++kk)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) dof[kk][j] = (_Float16)__uint_as_float(f.dob[kk][j] << 16);
-#pragma unroll
-            for (int mt = 0; mt < NKT; ++mt) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NK2; ++kk) acc = mfma32(f.qt[mt][kk], dof[kk], acc);
-                sF[buf][mt][lane] = acc;
-            }
-        };
-        F fa, fb;
-        if (NC > 0) {
-            fetch(NC - 1, fa);
-            fetch(NC - 2, fb);
-            compute(fa, 0);
-            fetch(NC - 3, fa);
-        }
-        // iteration j (chunk NC-1-j on wave 0) prepares chunk NC-2-j
-        auto step = [&](int j, F& f) __attribute__((always_inline)) {
-            lds_barrier();
-            const int c = NC - 2 - j;
-            if (c >= 0) {
-                compute(f, (j + 1) & 1);
-                fetch(c - 2, f);
-            }
-        };
-        for (int j = 0; j < NC; j += 2) {
-            step(j, fb);
-            if (j + 1 < NC) step(j + 1, fa);
-        }
-        return;
-    }
-
-    // ---------------------------------------------------- wave 0: D, backwards
-    using F = DFrags<DK, NK2>;
-    floatx4 D[NKT];
-#pragma unroll
-    for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            D[mt][i] = p.dSf ? p.dSf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] : 0.f;
-    auto fetch_kg = [&](int c, F& f) __attribute__((always_inline)) {
-        const unsigned char* rec = recp(c);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int rt = 0; rt < NB; ++rt) f.kw[kk][rt] = frag(rec, R::KW + (size_t)(rt * NKK + kk) * 1024);
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt) f.gm[mt] = *reinterpret_cast<const floatx4*>(rec + R::G + (16 * mt + g4) * 4);
-        f.flag = *reinterpret_cast<const int*>(rec + R::G + DK * 4);
-    };
-    auto fetch_w = [&](int c, F& f) __attribute__((always_inline)) {
-        const unsigned char* rec = recp(c);
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-            for (int kk = 0; kk < NK2; ++kk) f.wt[mt][kk] = frag(rec, R::WT + (size_t)(mt * NK2 + kk) * 1024);
-    };
-    F fa, fb;
-    if (NC > 0) {
-        fetch_kg(NC - 1, fa); fetch_w(NC - 1, fa);
-        fetch_kg(NC - 2, fb); fetch_w(NC - 2, fb);
-    }
-    bool poisoned = false;
-    const float qnan = __builtin_nanf("");
-    auto step = [&](int j, F& f) __attribute__((always_inline)) {
-        const int c = NC - 1 - j;
-        // the gradient of this chunk's end state, for the gradient kernel
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.dstates[(((size_t)bh * NC + c) * DK + 16 * mt + g4 + i) * DV + col] = poisoned ? qnan : D[mt][i];
-        if (f.flag) poisoned = true;
-        // Z = Kh D
-        half8 df[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) df[kk] = cat8(to_h4(D[2 * kk]), to_h4(D[2 * kk + 1]));
-        floatx4 Z[NB];
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Z[rt] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int rt = 0; rt < NB; ++rt) Z[rt] = mfma32(f.kw[kk][rt], df[kk], Z[rt]);
-        lds_barrier();                                   // F of chunk c is published
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt) D[mt] += sF[j & 1][mt][lane];
-        // D += -W^T Z, then D = diag(gamma) D
-        half8 zf[NK2];
-#pragma unroll
-        for (int kk = 0; kk < NK2; ++kk) zf[kk] = cat8(to_h4(-Z[2 * kk]), to_h4(-Z[2 * kk + 1]));
-#pragma unroll
-        for (int kk = 0; kk < NK2; ++kk)
-#pragma unroll
-            for (int mt = 0; mt < NKT; ++mt) D[mt] = mfma32(f.wt[mt][kk], zf[kk], D[mt]);
-        const floatx4* gm = f.gm;
-        floatx4 g2[NKT];
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt) g2[mt] = gm[mt];
-        fetch_kg(c - 2, f);
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt) D[mt] = D[mt] * g2[mt];
-        fetch_w(c - 2, f);
-    };
-    for (int j = 0; j < NC; j += 2) {
-        step(j, fa);
-        if (j + 1 < NC) step(j + 1, fb);
-    }
-    if (p.dS0) {
-#pragma unroll
-        for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.dS0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col] = poisoned ? qnan : D[mt][i];
-    }
-}
-
-template <int DK, int DV>
-static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t st) {
-    hipLaunchKernelGGL((dchain_kernel<DK, DV>), dim3((unsigned)(p.BH * (DV / 16))), dim3(128), 0, st, p,
-                       reinterpret_cast<const unsigned char*>(ws));
-    return hipGetLastError();
 }
 
 constexpr int kChainStrips = 1;
@@ -1174,10 +910,5 @@ hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st) {
-    if (dk == 128 && dv == 128) return wy::launch_dchain<128, 128>(p, records, st);
-    if (dk == 64 && dv == 64) return wy::launch_dchain<64, 64>(p, records, st);
-    return hipErrorInvalidValue;
-}
 
 }  // namespace gdr

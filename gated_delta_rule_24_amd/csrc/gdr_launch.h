@@ -33,7 +33,10 @@ struct FwdParams {
     const float* S0;       // may be null
     void* o;               // may be null (state-only passes)
     float* Sf;             // may be null
-    float* states;         // optional: chunk-start states [BH][NC][DK][DV] (backward recompute)
+    float* states;         // optional: chunk-start states [BH][NC][DK][DV] (backward recompute,
+                           // generic forward)
+    void* state_frags;     // optional: decayed chunk-start states S' as f16 fragments
+                           // (backward recompute, two-pass forward; wy::StateFrag layout)
     int BH;
     int T;
     uint32_t flags;
@@ -77,9 +80,11 @@ struct BwdParams {
     float* db;
     float* dw;
     float* dS0;
-    float* states;         // workspace: chunk-start states
-    float* dstates;        // workspace: state gradients at chunk ends
+    float* states;         // workspace: chunk-start states (generic path, fp32)
+    float* dstates;        // workspace: state gradients at chunk ends (generic path, fp32)
     void* records;         // workspace: per-chunk WY operands of the two-pass forward (or null)
+    void* state_frags;     // workspace, two-pass path: S' per chunk, f16 fragments
+    void* dstate_frags;    // workspace, two-pass path: chunk-end state gradients, f16 fragments
     int BH;
     int T;
     uint32_t flags;
@@ -88,6 +93,8 @@ struct BwdParams {
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
 // Reverse state-gradient chain over the records of launch_fwd_wy(..., bwd_layouts = true).
 hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st);
+// Per-chunk gradients over those records and the f16 state fragments.
+hipError_t launch_bwd_wgrad(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st);
 // split of that workspace: states, then state gradients, then the forward records
 size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
 bool bwd_supported(int dk, int dv, int chunk, uint32_t flags);

@@ -103,13 +103,14 @@ def test_decode_argument_validation():
 
 def test_bwd_workspace_query_and_validation():
     lib = _lib()
-    # chunk-start states and chunk-end gradients (2 x B*H x T/chunk x d_k x d_v fp32),
-    # plus the two-pass forward's records where that forward recomputes the states,
-    # each extended by three 64 x d_k f16 operand layouts for the reverse chain
-    states = 2 * 2 * 2 * 128 * 128 * 4
+    # the two-pass path: decayed chunk-start states and chunk-end gradients as f16
+    # (2 x B*H x T/chunk x d_k x d_v x 2 bytes), plus the forward's records, each
+    # extended by three 64 x d_k and two 64 x 64 f16 operand layouts for the
+    # backward passes
+    states = 2 * 2 * 2 * 128 * 128 * 2
     records = lib.gdr_chunk_fwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0)
     assert records > 0
-    extra = 2 * 2 * 3 * 64 * 128 * 2
+    extra = 2 * 2 * (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2)
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0) == states + records + extra
     # fp32 activations block the backward with chunks of 32
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 64, 1) == 2 * 2 * 4 * 64 * 64 * 4
