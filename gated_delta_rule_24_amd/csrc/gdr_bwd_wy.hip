@@ -207,7 +207,7 @@ static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t 
 // ---------------------------------------------------------------------------
 // Per-chunk gradients
 // ---------------------------------------------------------------------------
-// One workgroup of four waves per chunk, all chunks in parallel.  Inputs: the
+// One workgroup of d/16 waves per chunk, all chunks in parallel.  Inputs: the
 // chunk's record, its decayed start state S' and its end-state gradient D (f16
 // fragments), dO and the activations.  With U = Ũ - W S', dU = Kh D + P^T dO and
 // dR = T^T dU (the reverse of the triangular solve):
@@ -219,12 +219,13 @@ static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t 
 //   Phi = rowsum(dS' ⊙ S'),  dS' = D + Qs^T dO - E^T dR,
 // computed as rowsum(D ⊙ S') + colsum(Qs ⊙ dO S'^T) - colsum(E ⊙ dR S'^T), so
 // that dS' itself is never formed.
-// Phase A splits the value columns over the waves: U, dU, dR, and from dR the
-// value-side gradients dv = dR ⊙ w, dw = dR ⊙ v.  U, dR and dO go to LDS with
-// tokens as rows.  Phase B splits the channels: the value reductions
-// S' dO^T, S' dR^T and D U^T (channel x token accumulators), Phi, and the
-// small dP and dA.  Phase C adds the token reductions and forms the
-// element-wise gradients of q, k, b and log alpha in the same channel split.
+// Phase A gives each wave one 16-column value tile: U, dU, dR, and from dR the
+// value-side gradients dv = dR ⊙ w, dw = dR ⊙ v.  The record fragments every
+// wave reads there (W, Kh, P^T, T^T) are copied to LDS once per workgroup.  U,
+// dR and dO go to LDS with tokens as rows.  Phases B and C give each wave one
+// 16-channel tile: phase B the value reductions S' dO^T, S' dR^T and D U^T
+// (channel x token accumulators), Phi, and the small dP and dA; phase C the
+// token reductions and the element-wise gradients of q, k, b and log alpha.
 // Register tiles change orientation on the MFMA unit (product with the
 // identity), so no operand is gathered from LDS with strided scalar reads.
 template <int D>
@@ -242,7 +243,13 @@ struct WgradLayout {
     static constexpr size_t endC = oAT + (size_t)C * LDP * 2;
     static constexpr int NW = D / 16;      // waves: one 16-column value tile (phase A) and
                                            // one 16-channel tile (phases B, C) each
-    static constexpr size_t oRed = endB > endC ? endB : endC;     // [3][NW][C] fp32
+    // the record's fragments every wave of phase A reads, copied once: W, Kh
+    // (rows, K = channels), then P^T and T^T (rows, K = tokens)
+    static constexpr size_t oFW = endB > endC ? endB : endC;
+    static constexpr size_t oFK = oFW + (size_t)C * D * 2;
+    static constexpr size_t oFT = oFK + (size_t)C * D * 2;        // P^T blocks, then T^T blocks
+    static constexpr size_t endF = oFT + (size_t)2 * C * C * 2;
+    static constexpr size_t oRed = endF;                          // [3][NW][C] fp32
     static constexpr size_t oPhi = oRed + (size_t)3 * NW * C * 4; // [NW] fp32
     static constexpr size_t bytes = oPhi + (size_t)NW * 4;
 };
@@ -261,20 +268,35 @@ __device__ __forceinline__ floatx4 splat4(float x) {
     f[0] = f[1] = f[2] = f[3] = x;
     return f;
 }
-__device__ __forceinline__ floatx4 shfl4(floatx4 v, int src, int width) {
-    floatx4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __shfl(v[i], src, width);
-    return r;
+// Cross-lane moves within the 16-lane rows of a wave (DPP; lanes whose source
+// falls outside the row read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
-// inclusive prefix sum over the 16 lanes of each lane group (lane & 15 order)
-__device__ __forceinline__ floatx4 scan16(floatx4 x, int r16) {
+// inclusive prefix sum over the 16 lanes of each row (lane & 15 order)
+__device__ __forceinline__ floatx4 scan16(floatx4 x) {
 #pragma unroll
-    for (int d = 1; d < 16; d *= 2) {
-        floatx4 y;
+    for (int i = 0; i < 4; ++i) {
+        float v = x[i];
+        v += dpp<0x111>(v);     // row_shr:1
+        v += dpp<0x112>(v);     // row_shr:2
+        v += dpp<0x114>(v);     // row_shr:4
+        v += dpp<0x118>(v);     // row_shr:8
+        x[i] = v;
+    }
+    return x;
+}
+// sum over the 16 lanes of each row, the same bits in every lane
+__device__ __forceinline__ floatx4 rowsum16(floatx4 x) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = __shfl_up(x[i], d, 16);
-        if (r16 >= d) x += y;
+    for (int i = 0; i < 4; ++i) {
+        float v = x[i];
+        v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]
+        v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]
+        v += dpp<0x141>(v);     // row_half_mirror
+        v += dpp<0x140>(v);     // row_mirror
+        x[i] = v;
     }
     return x;
 }
@@ -286,18 +308,14 @@ __device__ __forceinline__ floatx4 expv4(floatx4 x) {
 }
 
 // g - g_C for the four channels 4g..4g+3 of a 16-channel tile (or the scalar
-// decay) at tokens 16 tt + r, tt < 4: the in-chunk prefix of log alpha over the
-// lanes of each group and across the four token tiles
-template <int D, bool AS>
-__device__ __forceinline__ void chunk_decay(const float* lag, int ch0, int r16, floatx4 (&gm)[4]) {
+// decay) at tokens 16 tt + r, tt < 4, from log alpha at those positions: the
+// in-chunk prefix over the lanes of each row and across the four token tiles
+__device__ __forceinline__ void chunk_decay(const floatx4 (&la)[4], floatx4 (&gm)[4]) {
     floatx4 carry = zero4();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + r16;
-        const floatx4 la = AS ? splat4(lag[t]) : *reinterpret_cast<const floatx4*>(lag + t * D + ch0);
-        const floatx4 x = scan16(la, r16);
-        gm[tt] = x + carry;
-        carry += shfl4(x, 15, 16);
+        gm[tt] = scan16(la[tt]) + carry;
+        carry += rowsum16(la[tt]);
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) gm[tt] -= carry;
@@ -309,10 +327,10 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     using SFB = StateFrag<D, D>;
     using L = WgradLayout<D>;
     constexpr size_t RB = R::bwd_bytes;
-    constexpr int NW = L::NW, TPW = 1, NKK = D / 32, NB = C / 16, NK2 = C / 32;
+    constexpr int NW = L::NW, NKK = D / 32, NB = C / 16, NK2 = C / 32;
     constexpr int LDX = L::LDX, LDP = L::LDP;
-    static_assert(NW * 16 == D && L::bytes <= 64 * 1024, "layout");
-    __shared__ __align__(16) unsigned char smem[L::bytes];
+    static_assert(NW * 16 == D && L::bytes <= 160 * 1024, "layout");
+    extern __shared__ __align__(16) unsigned char smem[];
     _Float16* sU = reinterpret_cast<_Float16*>(smem + L::oU);
     _Float16* sR = reinterpret_cast<_Float16*>(smem + L::oR);
     _Float16* sO = reinterpret_cast<_Float16*>(smem + L::oO);
@@ -355,118 +373,118 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     };
     const float poison = *reinterpret_cast<const int*>(rec + R::G + D * 4) ? __builtin_nanf("") : 0.f;
 
-    // ================= phase A: value columns 16 (TPW wave + j) .. +15, all tokens
-    floatx4 Y[TPW][NB], Z[TPW][NB];      // W S' and Kh D (+ P^T dO)
+    // ================= phase A: value columns 16 vt .. 16 vt + 15 (vt = wave), all tokens
+    const int vt = wave, ct = wave;
+    // shared fragments into LDS (16-byte pieces, in record order)
+    {
+        constexpr int PW = C * D * 2 / 16, PT2 = 2 * C * C * 2 / 16, NPC = 2 * PW + PT2;
+        constexpr int PER = (NPC + 64 * NW - 1) / (64 * NW);
+        uint4 cp[PER];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+        for (int m = 0; m < PER; ++m) {
+            const int pc = min(tid + 64 * NW * m, NPC - 1);
+            const size_t src = pc < PW ? R::W + (size_t)pc * 16
+                             : pc < 2 * PW ? R::KW + (size_t)(pc - PW) * 16 : R::PT + (size_t)(pc - 2 * PW) * 16;
+            cp[m] = *reinterpret_cast<const uint4*>(rec + src);
+        }
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Y[j][rt] = Z[j][rt] = zero4();
+        for (int m = 0; m < PER; ++m) {
+            const int pc = tid + 64 * NW * m;
+            if (pc < NPC) *reinterpret_cast<uint4*>(smem + L::oFW + (size_t)pc * 16) = cp[m];
+        }
+    }
+    auto lfrag = [&](size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(smem + off + lo16);
+    };
+    // inputs needed late in this phase: v and w for dv, dw; dO
+    uint2 vr[NB], wr[NB], dor[NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+        const int t = 16 * rt + r16, ix = t * D + 16 * vt + g4;
+        vr[rt] = *reinterpret_cast<const uint2*>(vg + ix);
+        if constexpr (WS) wr[rt].x = wg[t];
+        else wr[rt] = *reinterpret_cast<const uint2*>(wg + ix);
+        dor[rt] = *reinterpret_cast<const uint2*>(og + ix);
+    }
+    // Ũ (this wave's value tile) and the state fragments of the channel loop
+    half8 fur[NK2], fsa[NKK], fda[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NK2; ++kk) fur[kk] = frag(rec, R::U + (size_t)(vt * NK2 + kk) * 1024);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-        half8 fw[NB], fk[NB], fs[TPW], fd[TPW];
+        fsa[kk] = frag(sfr, SFB::block(vt, kk));
+        fda[kk] = frag(dfr, SFB::block(vt, kk));
+    }
+    lds_barrier();
+    // Y = W S' and Z = Kh D over the channels
+    floatx4 Y[NB], Z[NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) Y[rt] = Z[rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
-            fw[rt] = frag(rec, R::W + (size_t)(rt * NKK + kk) * 1024);
-            fk[rt] = frag(rec, R::KW + (size_t)(rt * NKK + kk) * 1024);
+            Y[rt] = mfma32(lfrag(L::oFW + (size_t)(rt * NKK + kk) * 1024), fsa[kk], Y[rt]);
+            Z[rt] = mfma32(lfrag(L::oFK + (size_t)(rt * NKK + kk) * 1024), fda[kk], Z[rt]);
         }
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            fs[j] = frag(sfr, SFB::block(TPW * wave + j, kk));
-            fd[j] = frag(dfr, SFB::block(TPW * wave + j, kk));
-        }
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int rt = 0; rt < NB; ++rt) {
-                Y[j][rt] = mfma32(fw[rt], fs[j], Y[j][rt]);
-                Z[j][rt] = mfma32(fk[rt], fd[j], Z[j][rt]);
-            }
-        __builtin_amdgcn_sched_barrier(0);
     }
     // dO: rows to LDS, and columns (K = tokens) for P^T dO
-    half8 dov[TPW][NK2];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int vt = TPW * wave + j;
+    half8 dov[NK2];
+    {
         floatx4 tq[NB];
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const int ix = (16 * st + r16) * D + 16 * vt + g4;
-            const half4 h = bf16x4_to_h4(*reinterpret_cast<const uint2*>(og + ix));
+            const half4 h = bf16x4_to_h4(dor[st]);
             *reinterpret_cast<half4*>(sO + (16 * st + r16) * LDX + 16 * vt + g4) = h;
             tq[st] = swap16(h, id);
         }
 #pragma unroll
-        for (int kk = 0; kk < NK2; ++kk) dov[j][kk] = cat8(to_h4(tq[2 * kk]), to_h4(tq[2 * kk + 1]));
+        for (int kk = 0; kk < NK2; ++kk) dov[kk] = cat8(to_h4(tq[2 * kk]), to_h4(tq[2 * kk + 1]));
     }
-    __builtin_amdgcn_sched_barrier(0);
     // dU = Kh D + P^T dO  (P^T blocks left of the diagonal pair are zero)
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-        for (int kk = rt / 2; kk < NK2; ++kk) {
-            const half8 fpt = frag(rec, R::PT + (size_t)(rt * NK2 + kk) * 1024);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) Z[j][rt] = mfma32(fpt, dov[j][kk], Z[j][rt]);
-        }
-    __builtin_amdgcn_sched_barrier(0);
+        for (int kk = rt / 2; kk < NK2; ++kk)
+            Z[rt] = mfma32(lfrag(L::oFT + (size_t)(rt * NK2 + kk) * 1024), dov[kk], Z[rt]);
     // dR = T^T dU
-    half8 duf[TPW][NK2];
+    half8 duf[NK2];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
-#pragma unroll
-        for (int kk = 0; kk < NK2; ++kk) duf[j][kk] = cat8(to_h4(Z[j][2 * kk]), to_h4(Z[j][2 * kk + 1]));
-    floatx4 dR[TPW][NB];
+    for (int kk = 0; kk < NK2; ++kk) duf[kk] = cat8(to_h4(Z[2 * kk]), to_h4(Z[2 * kk + 1]));
+    floatx4 dR[NB];
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
+        dR[rt] = zero4();
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) dR[j][rt] = zero4();
-#pragma unroll
-        for (int kk = rt / 2; kk < NK2; ++kk) {
-            const half8 ftt = frag(rec, R::TT + (size_t)(rt * NK2 + kk) * 1024);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) dR[j][rt] = mfma32(ftt, duf[j][kk], dR[j][rt]);
-        }
+        for (int kk = rt / 2; kk < NK2; ++kk)
+            dR[rt] = mfma32(lfrag(L::oFT + (size_t)(NB * NK2 + rt * NK2 + kk) * 1024), duf[kk], dR[rt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
     // U = Ũ - W S'  -> LDS rows (tokens)
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int vt = TPW * wave + j;
+    for (int kk = 0; kk < NK2; ++kk) {
+        const half8 ur = fur[kk];
 #pragma unroll
-        for (int kk = 0; kk < NK2; ++kk) {
-            const half8 ur = frag(rec, R::U + (size_t)(vt * NK2 + kk) * 1024);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rt = 2 * kk + h;
-                const floatx4 u = f4(h ? hi4(ur) : lo4(ur)) - Y[j][rt];
-                const floatx4 ut = swap16(to_h4(u), id);
-                *reinterpret_cast<half4*>(sU + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(ut);
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int rt = 2 * kk + h;
+            const floatx4 u = f4(h ? hi4(ur) : lo4(ur)) - Y[rt];
+            *reinterpret_cast<half4*>(sU + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(swap16(to_h4(u), id));
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
     // dR -> LDS rows; dv = dR ⊙ w and dw = dR ⊙ v from the row layout (fp32:
     // the transposed f16 value plus the transposed f16 remainder)
     float dwp[NB];
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) dwp[rt] = 0.f;
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int vt = TPW * wave + j;
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-            const half4 hi = to_h4(dR[j][rt]);
-            const floatx4 t1 = swap16(hi, id);
-            *reinterpret_cast<half4*>(sR + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(t1);
-            const floatx4 x = mfma16(to_h4(dR[j][rt] - f4(hi)), id, t1);
-            const int t = 16 * rt + r16, ix = t * D + 16 * vt + g4;
-            const floatx4 v4 = load_act4<false>(vg, ix);
-            const floatx4 w4 = WS ? splat4(bf16_to_f32(wg[t])) : load_act4<false>(wg, ix);
-            *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
-            if constexpr (WS) dwp[rt] += hsum4(x * v4);
-            else *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
-        }
+    for (int rt = 0; rt < NB; ++rt) {
+        const half4 hi = to_h4(dR[rt]);
+        const floatx4 t1 = swap16(hi, id);
+        *reinterpret_cast<half4*>(sR + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(t1);
+        const floatx4 x = mfma16(to_h4(dR[rt] - f4(hi)), id, t1);
+        const int ix = (16 * rt + r16) * D + 16 * vt + g4;
+        const floatx4 v4 = cvt_raw4<false>(Raw4<false>{vr[rt]});
+        const floatx4 w4 = WS ? splat4(bf16_to_f32((uint16_t)wr[rt].x)) : cvt_raw4<false>(Raw4<false>{wr[rt]});
+        *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
+        if constexpr (WS) dwp[rt] = hsum4(x * v4);
+        else *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
     }
     if constexpr (WS) {
 #pragma unroll
@@ -477,74 +495,85 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
             if (g4 == 0) sRed[(0 * NW + wave) * C + 16 * rt + r16] = v;
         }
     }
+    // the element-wise inputs of this wave's channels (16 ct .. 16 ct + 15), loaded
+    // now and kept to the end
+    floatx4 lar[NB];
+    uint2 qr[NB], kr[NB], brw[NB];
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+        const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
+        lar[tt] = AS ? splat4(lag[t]) : *reinterpret_cast<const floatx4*>(lag + ix);
+        qr[tt] = *reinterpret_cast<const uint2*>(qg + ix);
+        kr[tt] = *reinterpret_cast<const uint2*>(kg + ix);
+        if constexpr (BS) brw[tt].x = bg[t];
+        else brw[tt] = *reinterpret_cast<const uint2*>(bg + ix);
+    }
+    // phase B's state fragments: value tiles 2 kv + e, the channel pair holding ct
+    half8 fsb[NKK][2], fdb[NKK][2];
+#pragma unroll
+    for (int kv = 0; kv < NKK; ++kv)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            fsb[kv][e] = frag(sfr, SFB::block(2 * kv + e, ct >> 1));
+            fdb[kv][e] = frag(dfr, SFB::block(2 * kv + e, ct >> 1));
+        }
     lds_barrier();
 
-    // ================= phase B: channels 16 (TPW wave + j) .. +15, all tokens
+    // ================= phase B: channels 16 ct .. 16 ct + 15, all tokens
     // Per 32-column step kv: S' and D with K = value columns (rows of the state,
     // from the column fragments by the identity product), rowsum(D ⊙ S'), and
     // A1 = S' dO^T, A2 = S' dR^T, A3 = D U^T  (rows = channels, columns = tokens)
-    floatx4 A1[TPW][NB], A2[TPW][NB], A3[TPW][NB];
-    float phd[TPW];
+    floatx4 A1[NB], A2[NB], A3[NB];
+    float phd = 0.f;
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        phd[j] = 0.f;
+    for (int tt = 0; tt < NB; ++tt) A1[tt] = A2[tt] = A3[tt] = zero4();
+    {
+        const int h = ct & 1;
 #pragma unroll
-        for (int tt = 0; tt < NB; ++tt) A1[j][tt] = A2[j][tt] = A3[j][tt] = zero4();
-    }
-#pragma unroll
-    for (int kv = 0; kv < NKK; ++kv) {
-        half8 sc[TPW], dc[TPW];
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int ct = TPW * wave + j, kk = ct >> 1, h = ct & 1;
+        for (int kv = 0; kv < NKK; ++kv) {
             floatx4 xs[2], xd[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const half8 fs = frag(sfr, SFB::block(2 * kv + e, kk));
-                const half8 fd = frag(dfr, SFB::block(2 * kv + e, kk));
+                const half8 fs = fsb[kv][e], fd = fdb[kv][e];
                 xs[e] = swap16(h ? hi4(fs) : lo4(fs), id);    // S'[16ct + r][32kv + 16e + 4g + i]
                 xd[e] = swap16(h ? hi4(fd) : lo4(fd), id);
-                phd[j] += hsum4(xs[e] * xd[e]);
+                phd += hsum4(xs[e] * xd[e]);
             }
-            sc[j] = cat8(to_h4(xs[0]), to_h4(xs[1]));
-            dc[j] = cat8(to_h4(xd[0]), to_h4(xd[1]));
-        }
+            const half8 sc = cat8(to_h4(xs[0]), to_h4(xs[1]));
+            const half8 dc = cat8(to_h4(xd[0]), to_h4(xd[1]));
 #pragma unroll
-        for (int tt = 0; tt < NB; ++tt) {
-            const int off = (16 * tt + r16) * LDX + 32 * kv + g4;
-            const half8 bo = cat8(ld_h4(sO + off), ld_h4(sO + off + 16));
-            const half8 br = cat8(ld_h4(sR + off), ld_h4(sR + off + 16));
-            const half8 bu = cat8(ld_h4(sU + off), ld_h4(sU + off + 16));
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                A1[j][tt] = mfma32(sc[j], bo, A1[j][tt]);
-                A2[j][tt] = mfma32(sc[j], br, A2[j][tt]);
-                A3[j][tt] = mfma32(dc[j], bu, A3[j][tt]);
+            for (int tt = 0; tt < NB; ++tt) {
+                const int off = (16 * tt + r16) * LDX + 32 * kv + g4;
+                A1[tt] = mfma32(sc, cat8(ld_h4(sO + off), ld_h4(sO + off + 16)), A1[tt]);
+                A2[tt] = mfma32(sc, cat8(ld_h4(sR + off), ld_h4(sR + off + 16)), A2[tt]);
+                A3[tt] = mfma32(dc, cat8(ld_h4(sU + off), ld_h4(sU + off + 16)), A3[tt]);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
     // dP^T and dA^T tiles (s-tile st <= t-tile tt): Res[s][t] = sum_v U[s][v] X[t][v]
     // with X = dO (dP) or dR (-dA); twenty tiles over the waves
     constexpr int NPA = 2 * NB * (NB + 1) / 2, PAW = (NPA + NW - 1) / NW;
+    auto pa_tile = [&](int it, int& kind, int& st, int& tt) __attribute__((always_inline)) {
+        kind = it / (NPA / 2);
+        int t = it % (NPA / 2);
+        tt = 0;
+        while (t > tt) { t -= tt + 1; ++tt; }
+        st = t;
+    };
     floatx4 pa[PAW];
 #pragma unroll
     for (int m = 0; m < PAW; ++m) {
-        const int it = wave + NW * m, kind = it / (NPA / 2);
         pa[m] = zero4();
+        const int it = wave + NW * m;
         if (it >= NPA) break;
-        int t = it % (NPA / 2), tt = 0;
-        while (t > tt) { t -= tt + 1; ++tt; }
-        const int st = t;
+        int kind, st, tt;
+        pa_tile(it, kind, st, tt);
         const _Float16* xs = kind ? sR : sO;
-        floatx4 acc = zero4();
 #pragma unroll
         for (int kv = 0; kv < NKK; ++kv) {
             const int ou = (16 * st + r16) * LDX + 32 * kv + g4, ox = (16 * tt + r16) * LDX + 32 * kv + g4;
-            acc = mfma32(cat8(ld_h4(sU + ou), ld_h4(sU + ou + 16)), cat8(ld_h4(xs + ox), ld_h4(xs + ox + 16)), acc);
+            pa[m] = mfma32(cat8(ld_h4(sU + ou), ld_h4(sU + ou + 16)), cat8(ld_h4(xs + ox), ld_h4(xs + ox + 16)), pa[m]);
         }
-        pa[m] = acc;
-        __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();          // U, dR, dO are no longer read: their space takes dP and dA
 
@@ -552,11 +581,10 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     // the diagonal tiles; tiles beyond the diagonal are zero
 #pragma unroll
     for (int m = 0; m < PAW; ++m) {
-        const int it = wave + NW * m, kind = it / (NPA / 2);
+        const int it = wave + NW * m;
         if (it >= NPA) break;
-        int t = it % (NPA / 2), tt = 0;
-        while (t > tt) { t -= tt + 1; ++tt; }
-        const int st = t;
+        int kind, st, tt;
+        pa_tile(it, kind, st, tt);
         floatx4 v = pa[m];
         if (st == tt) {
 #pragma unroll
@@ -582,48 +610,39 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
             *reinterpret_cast<half4*>(base + (16 * rt + row) * LDP + 16 * cb + 4 * q) = z4;
         }
     }
-    // element-wise part: g - g_C (in-chunk prefix over tokens), E, Qs, Phi, and the
-    // channel-row fragments of E and Qs (K = tokens) for the token reductions
-    floatx4 phi[TPW];
-    half8 ef[TPW][NK2], qf[TPW][NK2], kf[TPW][NK2];
+    // element-wise part, lane (r, g): token 16 tt + r, channels 16 ct + 4g .. +3:
+    // g - g_C, E, Qs, Kh, Phi, and the channel-row fragments of -E, Qs and Kh (K = tokens)
+    floatx4 gm[NB];
+    chunk_decay(lar, gm);
+    half8 ef[NK2], qf[NK2], kf[NK2];
+    floatx4 phi;
+    {
+        floatx4 p2 = zero4(), eT[NB], qT[NB], kT[NB];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int ct = TPW * wave + j;
-#pragma unroll
-        for (int kk = 0; kk < NK2; ++kk) kf[j][kk] = frag(rec, R::K + (size_t)(ct * NK2 + kk) * 1024);
-        floatx4 gm[NB];
-        chunk_decay<D, AS>(lag, 16 * ct + g4, r16, gm);
-        floatx4 p2 = zero4();
+        for (int tt = 0; tt < NB; ++tt) {
+            const floatx4 eg = expv4(gm[tt]);
+            const floatx4 q4 = cvt_raw4<false>(Raw4<false>{qr[tt]}), k4 = cvt_raw4<false>(Raw4<false>{kr[tt]});
+            const floatx4 b4 = BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]});
+            const floatx4 E = b4 * k4 * eg, Qs = q4 * eg, Kh = k4 * expv4(-gm[tt]);
+            p2 += Qs * A1[tt] - E * A2[tt];
+            eT[tt] = swap16(to_h4(-E), id);     // -E: the dA tiles hold -dA
+            qT[tt] = swap16(to_h4(Qs), id);
+            kT[tt] = swap16(to_h4(Kh), id);
+        }
 #pragma unroll
         for (int kk = 0; kk < NK2; ++kk) {
-            floatx4 eT[2], qT[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int tt = 2 * kk + h;
-                const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
-                const floatx4 eg = expv4(gm[tt]);
-                const floatx4 q4 = load_act4<false>(qg, ix), k4 = load_act4<false>(kg, ix);
-                const floatx4 b4 = BS ? splat4(bf16_to_f32(bg[t])) : load_act4<false>(bg, ix);
-                const floatx4 E = b4 * k4 * eg, Qs = q4 * eg;
-                p2 += Qs * A1[j][tt] - E * A2[j][tt];
-                eT[h] = swap16(to_h4(-E), id);     // -E: the dA tiles hold -dA
-                qT[h] = swap16(to_h4(Qs), id);
-            }
-            ef[j][kk] = cat8(to_h4(eT[0]), to_h4(eT[1]));
-            qf[j][kk] = cat8(to_h4(qT[0]), to_h4(qT[1]));
+            ef[kk] = cat8(to_h4(eT[2 * kk]), to_h4(eT[2 * kk + 1]));
+            qf[kk] = cat8(to_h4(qT[2 * kk]), to_h4(qT[2 * kk + 1]));
+            kf[kk] = cat8(to_h4(kT[2 * kk]), to_h4(kT[2 * kk + 1]));
         }
-        // Phi: the token sum over the 16 lanes of a group, plus rowsum(D ⊙ S')
-        // (held per channel r by all four lane groups after the reduction)
-#pragma unroll
-        for (int d = 1; d < 16; d *= 2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p2[i] += __shfl_xor(p2[i], d, 64);
-        float pd = phd[j];
+        // Phi: the token sum over the lanes of a row, plus rowsum(D ⊙ S') (per
+        // channel r in every lane group after the cross-group sum)
+        p2 = rowsum16(p2);
+        float pd = phd;
         pd += __shfl_xor(pd, 16, 64);
         pd += __shfl_xor(pd, 32, 64);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) phi[j][i] = p2[i] + __shfl(pd, g4 + i, 64);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) phi[i] = p2[i] + __shfl(pd, g4 + i, 64);
     }
     lds_barrier();
 
@@ -636,65 +655,44 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
 #pragma unroll
         for (int kk = 0; kk < NK2; ++kk) {
             if (2 * kk <= tt) {
-                const half8 bp = cat8(ld_h4(sP + row + 32 * kk), ld_h4(sP + row + 32 * kk + 16));
-                const half8 ba = cat8(ld_h4(sA + row + 32 * kk), ld_h4(sA + row + 32 * kk + 16));
-#pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    A1[j][tt] = mfma32(kf[j][kk], bp, A1[j][tt]);
-                    A2[j][tt] = mfma32(kf[j][kk], ba, A2[j][tt]);
-                }
+                A1[tt] = mfma32(kf[kk], cat8(ld_h4(sP + row + 32 * kk), ld_h4(sP + row + 32 * kk + 16)), A1[tt]);
+                A2[tt] = mfma32(kf[kk], cat8(ld_h4(sA + row + 32 * kk), ld_h4(sA + row + 32 * kk + 16)), A2[tt]);
             }
             if (2 * kk + 1 >= tt) {
-                const half8 bpt = cat8(ld_h4(sPT + row + 32 * kk), ld_h4(sPT + row + 32 * kk + 16));
-                const half8 bat = cat8(ld_h4(sAT + row + 32 * kk), ld_h4(sAT + row + 32 * kk + 16));
-#pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    A3[j][tt] = mfma32(ef[j][kk], bat, A3[j][tt]);
-                    A3[j][tt] = mfma32(qf[j][kk], bpt, A3[j][tt]);
-                }
+                A3[tt] = mfma32(ef[kk], cat8(ld_h4(sAT + row + 32 * kk), ld_h4(sAT + row + 32 * kk + 16)), A3[tt]);
+                A3[tt] = mfma32(qf[kk], cat8(ld_h4(sPT + row + 32 * kk), ld_h4(sPT + row + 32 * kk + 16)), A3[tt]);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 
     // element-wise gradients; lane (r, g): token 16 tt + r, channels 16 ct + 4g .. +3
-    float dbs[NB], dgs[NB], phs = 0.f;
+    float dbs[NB], dgs[NB];
+    floatx4 carry = zero4();
 #pragma unroll
-    for (int tt = 0; tt < NB; ++tt) dbs[tt] = dgs[tt] = 0.f;
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int ct = TPW * wave + j;
-        floatx4 carry = zero4();
-        phs += hsum4(phi[j]);
-        floatx4 gm[NB];
-        chunk_decay<D, AS>(lag, 16 * ct + g4, r16, gm);
-#pragma unroll
-        for (int tt = 0; tt < NB; ++tt) {
-            const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
-            const floatx4 eg = expv4(gm[tt]), ek = expv4(-gm[tt]);
-            const floatx4 q4 = load_act4<false>(qg, ix), k4 = load_act4<false>(kg, ix);
-            const floatx4 b4 = BS ? splat4(bf16_to_f32(bg[t])) : load_act4<false>(bg, ix);
-            const floatx4 dQs = A1[j][tt], dE = -A2[j][tt], dKh = A3[j][tt];
-            *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
-            *reinterpret_cast<floatx4*>(dkg + ix) = dE * b4 * eg + dKh * ek + poison;
-            const floatx4 dbv = dE * k4 * eg;
-            if constexpr (BS) dbs[tt] += hsum4(dbv);
-            else *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
-            const floatx4 dg = dE * (b4 * k4 * eg) + dQs * (q4 * eg) - dKh * (k4 * ek);
-            if constexpr (AS) {
-                dgs[tt] += hsum4(dg);
-            } else {
-                const floatx4 incl = scan16(dg, r16);
-                *reinterpret_cast<floatx4*>(dlag + ix) = phi[j] - (carry + (incl - dg)) + poison;
-                carry += shfl4(incl, 15, 16);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+    for (int tt = 0; tt < NB; ++tt) {
+        const int ix = (16 * tt + r16) * D + 16 * ct + g4;
+        const floatx4 eg = expv4(gm[tt]), ek = expv4(-gm[tt]);
+        const floatx4 q4 = cvt_raw4<false>(Raw4<false>{qr[tt]}), k4 = cvt_raw4<false>(Raw4<false>{kr[tt]});
+        const floatx4 b4 = BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]});
+        const floatx4 dQs = A1[tt], dE = -A2[tt], dKh = A3[tt];
+        *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
+        *reinterpret_cast<floatx4*>(dkg + ix) = dE * b4 * eg + dKh * ek + poison;
+        const floatx4 dbv = dE * k4 * eg;
+        if constexpr (BS) dbs[tt] = hsum4(dbv);
+        else *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
+        const floatx4 dg = dE * (b4 * k4 * eg) + dQs * (q4 * eg) - dKh * (k4 * ek);
+        if constexpr (AS) {
+            dgs[tt] = hsum4(dg);
+        } else {
+            // d log alpha = Phi - (exclusive prefix of dg over the tokens)
+            *reinterpret_cast<floatx4*>(dlag + ix) = phi - (carry + (scan16(dg) - dg)) + poison;
+            carry += rowsum16(dg);
         }
     }
     if constexpr (AS || BS) {
 #pragma unroll
         for (int tt = 0; tt < NB; ++tt) {
-            float vb = dbs[tt], vg2 = dgs[tt];
+            float vb = BS ? dbs[tt] : 0.f, vg2 = AS ? dgs[tt] : 0.f;
             vb += __shfl_xor(vb, 16, 64);
             vb += __shfl_xor(vb, 32, 64);
             vg2 += __shfl_xor(vg2, 16, 64);
@@ -706,7 +704,7 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         }
         // Phi summed over this wave's channels (each lane group holds the same sums)
         if constexpr (AS) {
-            float v = phs;
+            float v = hsum4(phi);
             v += __shfl_xor(v, 16, 64);
             v += __shfl_xor(v, 32, 64);
             if (lane == 0) sPhi[wave] = v;
@@ -744,7 +742,16 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
 template <int D, bool AS, bool BS, bool WS>
 static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t st) {
     const int NC = p.T / C;
-    hipLaunchKernelGGL((wgrad_kernel<D, AS, BS, WS>), dim3((unsigned)(p.BH * NC)), dim3(D * 4), 0, st, p,
+    auto k = wgrad_kernel<D, AS, BS, WS>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)WgradLayout<D>::bytes);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.BH * NC)), dim3(D * 4), WgradLayout<D>::bytes, st, p,
                        reinterpret_cast<const unsigned char*>(ws));
     return hipGetLastError();
 }
