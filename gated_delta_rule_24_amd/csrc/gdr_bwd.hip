@@ -31,6 +31,8 @@
 // operands with fp32 activations), accumulation and every element-wise step
 // in fp32.  The chunk-local operands are built in LDS by prep_chunk, which
 // both kernels share.
+#include <mutex>
+
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -870,6 +872,31 @@ bool bwd_supported(int dk, int dv, int chunk, uint32_t /*flags*/) {
     return dk == dv && (dk == 64 || dk == 128) && (chunk == 32 || chunk == 64);
 }
 
+// A second stream per device, at the default priority, for the backward's
+// reverse chain: it depends only on the WY records, so it runs beside the
+// forward state chain (both are sequential over the chunks and leave most of
+// each compute unit idle).  The fork and join go through events, so the
+// caller's stream sees the usual ordering and the pattern stays capturable.
+namespace {
+struct SideStream {
+    std::mutex m;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+SideStream& side_stream(int dev) {
+    static SideStream sides[kMaxSideDevices];
+    return sides[dev];
+}
+hipError_t side_init(SideStream& sd) {
+    if (sd.s) return hipSuccess;
+    hipError_t e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+    return e;
+}
+}  // namespace
+
 // the two-pass path keeps S' and the state gradients as f16 fragments, the
 // generic path as fp32 rows
 static bool bwd_two_pass(int dk, int dv, int T, int cb, uint32_t flags) {
@@ -914,9 +941,25 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
         // its chain the decayed chunk-start states), the reverse chain over those
         // records, then every chunk's gradients
         f.state_frags = p.state_frags;
-        e = launch_fwd_wy(f, dk, dv, p.records, st, true);
+        e = launch_fwd_wy(f, dk, dv, p.records, st, true, kWyPass);
         if (e != hipSuccess) return e;
-        e = launch_bwd_dchain(p, dk, dv, p.records, st);
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < kMaxSideDevices) {
+            SideStream& sd = side_stream(dev);
+            std::lock_guard<std::mutex> lk(sd.m);
+            e = side_init(sd);
+            if (e == hipSuccess) e = hipEventRecord(sd.fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(sd.s, sd.fork, 0);
+            if (e == hipSuccess) e = launch_bwd_dchain(p, dk, dv, p.records, sd.s);
+            if (e == hipSuccess) e = hipEventRecord(sd.join, sd.s);
+            if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, sd.join, 0);
+        } else {
+            e = launch_bwd_dchain(p, dk, dv, p.records, st);
+            if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);
+        }
         if (e != hipSuccess) return e;
         return launch_bwd_wgrad(p, dk, dv, p.records, st);
     }

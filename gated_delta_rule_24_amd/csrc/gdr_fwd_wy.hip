@@ -831,7 +831,7 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
 constexpr int kChainStrips = 1;
 
 template <int DK, int DV, bool AS, bool BS, bool WS, bool BL>
-static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
+static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int passes) {
     using LP = PrepLayout<DK, DV>;
     auto kp = wy_kernel<DK, DV, AS, BS, WS, BL>;
     auto ks = chain_kernel<DK, DV, kChainStrips>;
@@ -854,28 +854,33 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st) {
         }
     }
     const int gp = total < ncu ? total : ncu;
-    hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(LP::NT), LP::bytes, st, p,
-                       reinterpret_cast<unsigned char*>(ws));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ks, dim3((unsigned)(p.BH * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
-                       reinterpret_cast<const unsigned char*>(ws), RB);
-    return hipGetLastError();
+    if (passes & kWyPass) {
+        hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(LP::NT), LP::bytes, st, p,
+                           reinterpret_cast<unsigned char*>(ws));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (passes & kChainPass) {
+        hipLaunchKernelGGL(ks, dim3((unsigned)(p.BH * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
+                           reinterpret_cast<const unsigned char*>(ws), RB);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <int DK, int DV, bool BL>
-static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st) {
+static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st, int passes) {
     const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
     const int m = (as ? 4 : 0) | (bs ? 2 : 0) | (wsc ? 1 : 0);
     switch (m) {
-        case 0: return launch_t<DK, DV, false, false, false, BL>(p, ws, st);
-        case 1: return launch_t<DK, DV, false, false, true, BL>(p, ws, st);
-        case 2: return launch_t<DK, DV, false, true, false, BL>(p, ws, st);
-        case 3: return launch_t<DK, DV, false, true, true, BL>(p, ws, st);
-        case 4: return launch_t<DK, DV, true, false, false, BL>(p, ws, st);
-        case 5: return launch_t<DK, DV, true, false, true, BL>(p, ws, st);
-        case 6: return launch_t<DK, DV, true, true, false, BL>(p, ws, st);
-        default: return launch_t<DK, DV, true, true, true, BL>(p, ws, st);
+        case 0: return launch_t<DK, DV, false, false, false, BL>(p, ws, st, passes);
+        case 1: return launch_t<DK, DV, false, false, true, BL>(p, ws, st, passes);
+        case 2: return launch_t<DK, DV, false, true, false, BL>(p, ws, st, passes);
+        case 3: return launch_t<DK, DV, false, true, true, BL>(p, ws, st, passes);
+        case 4: return launch_t<DK, DV, true, false, false, BL>(p, ws, st, passes);
+        case 5: return launch_t<DK, DV, true, false, true, BL>(p, ws, st, passes);
+        case 6: return launch_t<DK, DV, true, true, false, BL>(p, ws, st, passes);
+        default: return launch_t<DK, DV, true, true, true, BL>(p, ws, st, passes);
     }
 }
 
@@ -896,17 +901,18 @@ size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts) {
     return (size_t)BH * (size_t)(T / wy::C) * rec;
 }
 
-hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st, bool bwd_layouts) {
+hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st, bool bwd_layouts,
+                         int passes) {
     if (p.T == 0) return hipErrorInvalidValue;
     if (bwd_layouts) {
-        if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, true>(p, ws, st);
-        if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, true>(p, ws, st);
+        if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, true>(p, ws, st, passes);
+        if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, true>(p, ws, st, passes);
         return hipErrorInvalidValue;
     }
-    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false>(p, ws, st);
-    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false>(p, ws, st);
-    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false>(p, ws, st);
-    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false>(p, ws, st);
+    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false>(p, ws, st, passes);
+    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false>(p, ws, st, passes);
+    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false>(p, ws, st, passes);
+    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false>(p, ws, st, passes);
     return hipErrorInvalidValue;
 }
 

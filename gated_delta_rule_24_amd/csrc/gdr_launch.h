@@ -60,8 +60,10 @@ hipError_t launch_fwd_pipe(const FwdParams& p, int dk, int dv, hipStream_t st);
 // reads (d_k == d_v only).
 bool fwd_wy_supported(int dk, int dv, int chunk, uint32_t flags);
 size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts = false);
+// passes: the WY pass, the state chain, or both (in that order on st).
+constexpr int kWyPass = 1, kChainPass = 2;
 hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st,
-                         bool bwd_layouts = false);
+                         bool bwd_layouts = false, int passes = kWyPass | kChainPass);
 
 struct BwdParams {
     const void* q;

@@ -158,3 +158,37 @@ def test_gdn2_backward_full_workload_sampled_heads():
     _check(inp, got, _ref(inp, heads=heads), 2e-2, heads=heads)
     for n in GRADS:
         assert np.isfinite(got[n]).all(), n
+
+
+def test_backward_graph_capture_replays():
+    """The two-pass backward (its reverse chain forks onto a second stream and
+    joins back) captured into a graph replays to the eager result, on several
+    replays with eager work between them."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    inp = _case("graph", B=1, H=2, T=256, dk=128, dv=128)
+    d = to_dev(inp)
+    dsf = torch.from_numpy(_dsf(inp)).cuda()
+
+    def run():
+        return gdr.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"],
+                             dsf, chunk=64)
+    eager = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        x = torch.randn(1 << 20, device="cuda")
+        x.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(captured[n], eager[n]), (rep, n)
