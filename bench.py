@@ -62,6 +62,7 @@ BWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
 # the counters in the traffic summary are only used while these sources are
 # unchanged
 FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_wy.hip",
+                      "gated_delta_rule_24_amd/csrc/gdr_wy.h",
                       "gated_delta_rule_24_amd/csrc/gdr_device.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
 

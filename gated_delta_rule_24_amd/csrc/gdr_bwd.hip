@@ -889,10 +889,11 @@ SideStream& side_stream(int dev) {
     return sides[dev];
 }
 hipError_t side_init(SideStream& sd) {
-    if (sd.s) return hipSuccess;
-    hipError_t e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+    if (sd.s && sd.fork && sd.join) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (!sd.s) e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+    if (e == hipSuccess && !sd.fork) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+    if (e == hipSuccess && !sd.join) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
     return e;
 }
 }  // namespace
@@ -946,16 +947,24 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
         int dev = 0;
         e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < kMaxSideDevices) {
-            SideStream& sd = side_stream(dev);
-            std::lock_guard<std::mutex> lk(sd.m);
-            e = side_init(sd);
-            if (e == hipSuccess) e = hipEventRecord(sd.fork, st);
-            if (e == hipSuccess) e = hipStreamWaitEvent(sd.s, sd.fork, 0);
-            if (e == hipSuccess) e = launch_bwd_dchain(p, dk, dv, p.records, sd.s);
-            if (e == hipSuccess) e = hipEventRecord(sd.join, sd.s);
+        SideStream* sd = (dev >= 0 && dev < kMaxSideDevices) ? &side_stream(dev) : nullptr;
+        std::unique_lock<std::mutex> lk;
+        if (sd) {
+            lk = std::unique_lock<std::mutex>(sd->m);
+            if (side_init(*sd) != hipSuccess) {
+                // no second stream (e.g. first use inside a graph capture that forbids
+                // creating one): the reverse chain runs after the state chain instead
+                (void)hipGetLastError();
+                sd = nullptr;
+            }
+        }
+        if (sd) {
+            e = hipEventRecord(sd->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+            if (e == hipSuccess) e = launch_bwd_dchain(p, dk, dv, p.records, sd->s);
+            if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
             if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);
-            if (e == hipSuccess) e = hipStreamWaitEvent(st, sd.join, 0);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, sd->join, 0);
         } else {
             e = launch_bwd_dchain(p, dk, dv, p.records, st);
             if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);

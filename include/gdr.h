@@ -23,7 +23,9 @@
  * - All tensor pointers are DEVICE pointers owned by the caller.  The
  *   library never allocates device memory (scratch space is passed in as a
  *   caller-owned workspace), never frees caller memory, and keeps no state
- *   besides a lazily cached device-property record.
+ *   besides a lazily cached device-property record and, once the backward
+ *   has run on a device, one extra stream and two events there (kept until
+ *   the process ends).
  * - Execution is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL is the default stream).  No call synchronises.
  * - Arguments are validated before any launch.  An invalid argument returns
@@ -158,6 +160,11 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
  *   dS0        : [B, H, d_k, d_v]; may be NULL when not needed.
  *   workspace  : device scratch of at least gdr_chunk_bwd_workspace_bytes()
  *                bytes, owned by the caller; contents on entry are ignored.
+ * Part of the work may run on the library's second stream for the device; it
+ * waits for the work queued on `stream` before the call and `stream` waits for
+ * it before the call's last kernel (event fork and join), so every effect is
+ * ordered on `stream` as if it ran there, also under graph capture.  Calls on
+ * one device share that second stream.
  * Supported: bf16 or fp32 activations, d_k = d_v = 128 or 64, chunk 64 or
  * 32.  Returns GDR_ERR_UNSUPPORTED otherwise.
  */
