@@ -386,7 +386,8 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDT + 16 * blk + jc] = (_Float16)x[r];
         } else {
             // meanwhile: fragments of P (K = tokens) and Kh^T (K = tokens)
-            constexpr int NPB = NB * (C / 32), NKB = (DK / 16) * (C / 32);
+            // (the backward reads P^T instead: no P rows then)
+            constexpr int NPB = BL ? 0 : NB * (C / 32), NKB = (DK / 16) * (C / 32);
             for (int task = wave - 1; task < NPB + NKB; task += NT / 64 - 1) {
                 if (task < NPB) {
                     const int rt = task / (C / 32), kk = task % (C / 32);
@@ -506,7 +507,7 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 for (int h = 0; h < 2; ++h)
                     acc[h] = mfma32(cat8(fx[h][k], fx[h][k + 1]), cat8(fy[k], fy[k + 1]), acc[h]);
             const half4 q0 = to_h4(f4(fq[0]) - acc[0]), q1 = to_h4(f4(fq[1]) - acc[1]);
-            st_nt(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16, cat8(q0, q1));
+            if constexpr (!BL) st_nt(rec + R::Q + ((size_t)(rt * NKK + kk) * 64 + lane) * 16, cat8(q0, q1));
             if constexpr (BL) {
                 // Q̃^T [ch][t] into the (now free) E^T buffer for the channel-row fragments
 #pragma unroll
@@ -636,6 +637,40 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
             }
         };
         constexpr int TD = 5;
+        if (p.o == nullptr) {
+            // state-only pass (the backward's recompute): no output to form, only
+            // the L2 touches of the state wave's part of the records ahead of it,
+            // with one barrier per chunk as the state wave expects
+            constexpr int SLINE = (int)(R::state_bytes / 128);
+            constexpr int SPL = (SLINE + 64 * NGRP - 1) / (64 * NGRP);
+            static_assert(SPL <= LPL, "touch registers");
+            auto touch_s = [&](int c, uint32_t (&tr)[LPL]) __attribute__((always_inline)) {
+                const unsigned char* rec = recp(c);
+#pragma unroll
+                for (int r = 0; r < SPL; ++r) {
+                    tacc ^= tr[r];
+                    const int li = ng + NGRP * (lane + 64 * r);
+                    tr[r] = *reinterpret_cast<const uint32_t*>(rec + (size_t)(li < SLINE ? li : SLINE - 1) * 128);
+                }
+            };
+            if (NC > 0) {
+                touch_s(2, ta);
+                touch_s(3, tb);
+            }
+            for (int c = 0; c < NC; c += 2) {
+                lds_barrier();
+                touch_s(c + TD, ta);
+                if (c + 1 < NC) {
+                    lds_barrier();
+                    touch_s(c + 1 + TD, tb);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < LPL; ++r) tacc ^= ta[r] ^ tb[r];
+            // never true (flag bit 31 is rejected by the API); keeps the touch loads
+            if ((p.flags & 0x80000000u) && tacc == 0x12345u) p.Sf[0] = 0.f;
+            return;
+        }
         if (NC > 0) {
             touch(2, ta);
             touch(3, tb);
@@ -669,8 +704,7 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
             fetch(c + 2, f);                                 // operands two chunks ahead
             touch(c + TD, tr);
             // the tile goes through LDS (this wave only) so that each lane stores
-            // four consecutive columns of a row (state-only passes have no output)
-            if (p.o == nullptr) return;
+            // four consecutive columns of a row
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll

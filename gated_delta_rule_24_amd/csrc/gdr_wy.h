@@ -26,13 +26,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   G      e^{g_C} per channel (fp32), then an int flag (decay out of range)
 template <int DK, int DV>
 struct Rec {
+    // what the state wave of the chain reads first (W, Kh^T, Ũ, G), then what
+    // only the output wave reads (Q̃, P; not written when the backward runs)
     static constexpr size_t W = 0;
-    static constexpr size_t Q = W + (size_t)C * DK * 2;
-    static constexpr size_t K = Q + (size_t)C * DK * 2;
-    static constexpr size_t P = K + (size_t)DK * C * 2;
-    static constexpr size_t U = P + (size_t)C * C * 2;
+    static constexpr size_t K = W + (size_t)C * DK * 2;
+    static constexpr size_t U = K + (size_t)DK * C * 2;
     static constexpr size_t G = U + (size_t)C * DV * 2;
-    static constexpr size_t bytes = G + (((size_t)DK * 4 + 16 + 255) & ~size_t(255));
+    static constexpr size_t Q = G + (((size_t)DK * 4 + 16 + 255) & ~size_t(255));
+    static constexpr size_t state_bytes = Q;
+    static constexpr size_t P = Q + (size_t)C * DK * 2;
+    static constexpr size_t bytes = P + (size_t)C * C * 2;
     static constexpr size_t strip = (size_t)C * 16 * 2;   // Ũ bytes per 16-column strip
     // appended when the backward consumes the records:
     //   KW  block (rt, kk): row t = 16 rt + r of Kh, K = channels
