@@ -249,7 +249,13 @@ struct WgradLayout {
     static constexpr size_t oFK = oFW + (size_t)C * D * 2;
     static constexpr size_t oFT = oFK + (size_t)C * D * 2;        // P^T blocks, then T^T blocks
     static constexpr size_t endF = oFT + (size_t)2 * C * C * 2;
-    static constexpr size_t oRed = endF;                          // [3][NW][C] fp32
+    // after phase A the same space holds S' and D with channels as rows (phase B's
+    // operands, K = value columns): [D][LDS] f16 each
+    static constexpr int LDS = D + 8;
+    static constexpr size_t oSr = oFW;
+    static constexpr size_t oDr = oSr + (size_t)D * LDS * 2;
+    static constexpr size_t endS = oDr + (size_t)D * LDS * 2;
+    static constexpr size_t oRed = endF > endS ? endF : endS;     // [3][NW][C] fp32
     static constexpr size_t oPhi = oRed + (size_t)3 * NW * C * 4; // [NW] fp32
     static constexpr size_t bytes = oPhi + (size_t)NW * 4;
 };
@@ -508,39 +514,41 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         if constexpr (BS) brw[tt].x = bg[t];
         else brw[tt] = *reinterpret_cast<const uint2*>(bg + ix);
     }
-    // phase B's state fragments: value tiles 2 kv + e, the channel pair holding ct
-    half8 fsb[NKK][2], fdb[NKK][2];
+    lds_barrier();
+    // S' and D (this wave's value tile, all channels) into LDS with channels as
+    // rows, for phase B's value reductions (the shared fragments are dead now)
+    {
+        _Float16* sSr = reinterpret_cast<_Float16*>(smem + L::oSr);
+        _Float16* sDr = reinterpret_cast<_Float16*>(smem + L::oDr);
 #pragma unroll
-    for (int kv = 0; kv < NKK; ++kv)
+        for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            fsb[kv][e] = frag(sfr, SFB::block(2 * kv + e, ct >> 1));
-            fdb[kv][e] = frag(dfr, SFB::block(2 * kv + e, ct >> 1));
-        }
+            for (int h = 0; h < 2; ++h) {
+                const int off = (32 * kk + 16 * h + r16) * L::LDS + 16 * vt + g4;
+                *reinterpret_cast<half4*>(sSr + off) = to_h4(swap16(h ? hi4(fsa[kk]) : lo4(fsa[kk]), id));
+                *reinterpret_cast<half4*>(sDr + off) = to_h4(swap16(h ? hi4(fda[kk]) : lo4(fda[kk]), id));
+            }
+    }
     lds_barrier();
 
     // ================= phase B: channels 16 ct .. 16 ct + 15, all tokens
-    // Per 32-column step kv: S' and D with K = value columns (rows of the state,
-    // from the column fragments by the identity product), rowsum(D ⊙ S'), and
+    // Per 32-column step kv: S' and D with K = value columns (their rows, from
+    // LDS), rowsum(D ⊙ S'), and
     // A1 = S' dO^T, A2 = S' dR^T, A3 = D U^T  (rows = channels, columns = tokens)
     floatx4 A1[NB], A2[NB], A3[NB];
     float phd = 0.f;
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) A1[tt] = A2[tt] = A3[tt] = zero4();
     {
-        const int h = ct & 1;
+        const _Float16* sSr = reinterpret_cast<const _Float16*>(smem + L::oSr) + (16 * ct + r16) * L::LDS + g4;
+        const _Float16* sDr = reinterpret_cast<const _Float16*>(smem + L::oDr) + (16 * ct + r16) * L::LDS + g4;
 #pragma unroll
         for (int kv = 0; kv < NKK; ++kv) {
-            floatx4 xs[2], xd[2];
+            // S'[16ct + r][32kv + 4g + i] and [.. + 16 + ..], likewise D
+            const half8 sc = cat8(ld_h4(sSr + 32 * kv), ld_h4(sSr + 32 * kv + 16));
+            const half8 dc = cat8(ld_h4(sDr + 32 * kv), ld_h4(sDr + 32 * kv + 16));
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const half8 fs = fsb[kv][e], fd = fdb[kv][e];
-                xs[e] = swap16(h ? hi4(fs) : lo4(fs), id);    // S'[16ct + r][32kv + 16e + 4g + i]
-                xd[e] = swap16(h ? hi4(fd) : lo4(fd), id);
-                phd += hsum4(xs[e] * xd[e]);
-            }
-            const half8 sc = cat8(to_h4(xs[0]), to_h4(xs[1]));
-            const half8 dc = cat8(to_h4(xd[0]), to_h4(xd[1]));
+            for (int e = 0; e < 8; ++e) phd += (float)sc[e] * (float)dc[e];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt) {
                 const int off = (16 * tt + r16) * LDX + 32 * kv + g4;
