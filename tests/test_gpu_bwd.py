@@ -93,6 +93,11 @@ CASES = [
      2e-2, True),
     ("erase_range_0_2", dict(B=1, H=2, T=192, dk=128, dv=128, gate_hi=2.0), 2e-2, False),
     ("single_chunk", dict(B=2, H=1, T=64, dk=128, dv=128), 2e-2, True),
+    ("gdn_scalar_tied_d64", dict(B=1, H=2, T=192, dk=64, dv=64, alpha_mode="scalar",
+                                 b_mode="scalar", w_mode="scalar", tied=True), 2e-2, True),
+    ("alpha_scalar_d64", dict(B=2, H=1, T=128, dk=64, dv=64, alpha_mode="scalar"), 2e-2, False),
+    ("long_d64", dict(B=1, H=2, T=1024, dk=64, dv=64), 2e-2, True),
+    ("long_d128", dict(B=1, H=1, T=1024, dk=128, dv=128), 2e-2, True),
     ("f32_d128", dict(B=1, H=2, T=128, dk=128, dv=128, act="f32"), 1e-4, True),
     ("f32_d64_c32", dict(B=1, H=2, T=96, dk=64, dv=64, act="f32", chunk=32), 1e-4, False),
     ("f32_scalar_gdn", dict(B=1, H=2, T=96, dk=64, dv=64, act="f32", chunk=32, alpha_mode="scalar",
