@@ -17,13 +17,15 @@
 //   db = dE ⊙ k ⊙ e^{g-g_C}     dw = dX ⊙ v      dv = dX ⊙ w
 //   dq = dQs ⊙ e^{g-g_C}        dk = dE ⊙ b ⊙ e^{g-g_C} + dKh ⊙ e^{g_C-g}
 //
-// Three launches on the caller's stream:
-//   1. the forward kernels recompute every chunk-start state into the workspace
-//      (the two-pass forward where it applies, its records in the workspace too);
-//   2. the chunks are walked backwards carrying D (the columns of D are
-//      independent), storing each chunk-end gradient and finally dS0: with the
-//      two-pass records by the reverse chain of gdr_fwd_wy.hip, otherwise by
-//      dstate_kernel (one workgroup per head and block of 32 value columns);
+// Where the two-pass forward applies (bf16 activations, chunk 64), launch_bwd
+// runs its WY pass, then its state chain (recording each chunk's S') beside the
+// reverse chain of gdr_bwd_wy.hip on a second stream, then that file's
+// per-chunk gradient kernel.  Otherwise (fp32 activations, chunks of 32, or the
+// generic forward forced by flag), three launches on the caller's stream:
+//   1. the generic forward recomputes every chunk-start state into the workspace;
+//   2. dstate_kernel walks the chunks backwards carrying D (the columns of D
+//      are independent; one workgroup per head and block of 32 value columns),
+//      storing each chunk-end gradient and finally dS0;
 //   3. grad_kernel computes the gradients of every chunk from its S and D, one
 //      workgroup per (head, chunk), all chunks in parallel, with the value
 //      dimension reduced in a fixed order (deterministic, no atomics).

@@ -1,5 +1,10 @@
 // Backward passes over the two-pass forward's records (bf16 activations,
-// chunk 64, d_k = d_v in {64, 128}).
+// chunk 64, d_k = d_v in {64, 128}): the reverse chain that carries the
+// gradient of the state backwards through the chunks, and the per-chunk
+// gradients with separate erase and write gate gradients (the gate-aware
+// accumulation of the Gated DeltaNet-2 Q&A page, Q4).  The reverse-mode
+// formulas per chunk are those written out at the top of gdr_bwd.hip; here the
+// triangular factors come from the forward's records instead of being rebuilt.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 #include "gdr_wy.h"
