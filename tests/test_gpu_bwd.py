@@ -197,3 +197,14 @@ def test_backward_graph_capture_replays():
         torch.cuda.synchronize()
         for n in GRADS:
             assert torch.equal(captured[n], eager[n]), (rep, n)
+
+
+def test_gdn_backward_workload_shape_sampled_heads():
+    """The backward on the Gated DeltaNet workload's shape (B=4, H=16, T=2048, scalar
+    gates, one buffer for b and w, zero initial state), checked on sampled heads."""
+    inp = _case("gdn", with_dO=True)
+    got = _run(inp)
+    heads = [0, 37, 63]
+    _check(inp, got, _ref(inp, heads=heads), 2e-2, heads=heads)
+    for n in GRADS:
+        assert np.isfinite(got[n]).all(), n
