@@ -49,6 +49,7 @@ FWD_FLOPS_PER_TOKEN = 6 * FD * FD + 2 * FC * (3 * FD + 2 * FD)
 
 # decode workload
 DN, DH, DD = 256, 32, 128
+SMALL_DECODE_N = (1, 16)          # small-batch (latency) decode lines
 DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + DD * 2) + DD * 4
 
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
@@ -145,24 +146,27 @@ def bench_fwd(steps, warmup):
     return inp, wall_ms, ev_ms
 
 
-def bench_decode(steps, warmup):
+def bench_decode(steps, warmup, N=None):
+    """One decode step of N sequences x 32 heads (N defaults to the 256-sequence
+    workload; small N is the low-latency decode of a few sequences)."""
     import torch
     import gdr_synth as gs
     import gated_delta_rule_24_amd as gdr
-    S = torch.from_numpy(gs.decode_state(DN, DH, DD, DD, seed=0)).cuda()
+    N = DN if N is None else N
+    S = torch.from_numpy(gs.decode_state(N, DH, DD, DD, seed=0)).cuda()
     toks = []
     for st in range(8):
-        t = gs.decode_token(DN, DH, DD, DD, st, seed=0)
+        t = gs.decode_token(N, DH, DD, DD, st, seed=0)
         toks.append({n: torch.from_numpy(a).to(torch.float32 if n == "log_alpha"
                                                else torch.bfloat16).cuda() for n, a in t.items()})
-    o = torch.empty((DN, DH, DD), dtype=torch.float32, device="cuda")
+    o = torch.empty((N, DH, DD), dtype=torch.float32, device="cuda")
     i = [0]
 
     def step():
         t = toks[i[0] % 8]
         i[0] += 1
         gdr.gdr_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["b"], t["w"], S, o,
-                            DN, DH, DD, DD, 0)
+                            N, DH, DD, DD, 0)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
     return wall_ms, ev_ms
 
@@ -268,6 +272,12 @@ def main():
     dec_wall, dec_ev = bench_decode(max(args.steps, 10), args.warmup)
     dec_gbs = DN * DH * DEC_BYTES_PER_HEAD / (dec_ev * 1e-3) / 1e9
     log(f"decode: {dec_ev * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+    small = {}
+    for n in SMALL_DECODE_N:
+        _, ev = bench_decode(max(args.steps, 20), args.warmup, N=n)
+        small[f"N={n}"] = {"us_per_step": ev * 1e3,
+                           "GB_per_s": n * DH * DEC_BYTES_PER_HEAD / (ev * 1e-3) / 1e9}
+        log(f"decode N={n}: {ev * 1e3:.1f} us/step")
 
     bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
     bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
@@ -319,6 +329,7 @@ def main():
             "GB_per_s": dec_gbs,
             "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
             "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
+            "small_batch": {"workload": "decode H=32 d=128, N sequences (latency)", **small},
         },
         "backward": {
             "workload": "gdn2_chunk_bwd B=1 H=32 T=16384 d_k=d_v=128 chunk=64, dO only",

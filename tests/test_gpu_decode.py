@@ -28,6 +28,13 @@ CASES = [
     (3, 2, 32, 128, "f32", "channel", "scalar", "channel"),
     (3, 2, 128, 16, "bf16", "channel", "channel", "scalar"),
     (1, 1, 64, 32, "f32", "channel", "channel", "channel"),
+    # more heads, and a single one
+    (16, 32, 128, 128, "bf16", "channel", "channel", "channel"),
+    (10, 20, 128, 128, "bf16", "channel", "channel", "channel"),
+    (5, 20, 128, 128, "f32", "channel", "scalar", "channel"),
+    (1, 1, 128, 128, "f32", "scalar", "channel", "scalar"),
+    (10, 20, 64, 64, "bf16", "channel", "channel", "channel"),
+    (5, 20, 64, 64, "f32", "scalar", "scalar", "channel"),
 ]
 
 
