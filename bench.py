@@ -9,7 +9,8 @@ fp32 log-decay and state.  One step = one gdr_chunk_fwd call over that batch
 value = B*H*T head-tokens per second of wall time over the timed steps.
 
 Also reported in the same JSON line: the recurrent decode step (256
-sequences x 32 heads, fp32 state streamed in place) in GB/s, the backward
+sequences x 32 heads, fp32 state streamed in place) in GB/s, the same
+forward over packed documents of varied lengths, the backward
 (1 x 32 heads x 16384 tokens), the roofline position of the forward call
 (the method's algorithmic HBM bytes per call over the measured call
 duration, with the measured HBM traffic of both kernels), and the fp64 CPU
@@ -51,6 +52,11 @@ FWD_FLOPS_PER_TOKEN = 6 * FD * FD + 2 * FC * (3 * FD + 2 * FD)
 DN, DH, DD = 256, 32, 128
 SMALL_DECODE_N = (1, 16)          # small-batch (latency) decode lines
 DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + DD * 2) + DD * 4
+
+# packed-sequence forward workload: the headline's 16 heads x 16384 tokens per
+# head, cut into documents of long-tailed lengths (mean 1024) instead of two
+# sequences of 8192
+VH, VT, VMEAN = 16, 16384, 1024
 
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
 # head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
@@ -171,6 +177,47 @@ def bench_decode(steps, warmup, N=None):
     return wall_ms, ev_ms
 
 
+def varlen_lengths():
+    """Document lengths of the packed workload: long-tailed draws, the last
+    one cut so that they sum to VT."""
+    import gdr_synth as gs
+    out, tot = [], 0
+    for n in gs.packed_lengths(4 * VT // VMEAN, VMEAN, seed=0):
+        n = min(n, VT - tot)
+        out.append(n)
+        tot += n
+        if tot == VT:
+            return out
+    out.append(VT - tot)
+    return out
+
+
+def bench_varlen(steps, warmup):
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    lengths = varlen_lengths()
+    inp = gs.packed_inputs(lengths, VH, FD, FD, seed=0)
+    a = inp.arrays
+    d = {n: torch.from_numpy(np.ascontiguousarray(a[n][0])).to(
+        torch.float32 if n == "log_alpha" else torch.bfloat16).cuda()
+        for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    S0 = torch.from_numpy(a["S0"]).cuda()
+    cu = torch.from_numpy(a["cu_seqlens"]).cuda()
+    nseq = len(lengths)
+    o = torch.empty((VH, VT, FD), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((nseq, VH, FD, FD), dtype=torch.float32, device="cuda")
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    nbytes = gdr.gdr_chunk_fwd_varlen_workspace_bytes(nseq, VH, VT, FD, FD, flags)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdr.gdr_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0, o,
+                                 Sf, cu, nseq, VH, VT, FD, FD, flags, ws, nbytes)
+    wall_ms, ev_ms = time_loop(step, steps, warmup)
+    return lengths, wall_ms, ev_ms
+
+
 def bench_copy(steps, warmup):
     """Plain 1 GiB device copy, the calibration kernel for HBM counters."""
     import torch
@@ -229,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen"], default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -252,6 +299,10 @@ def main():
     if args.only == "decode":
         w, e = bench_decode(args.steps, args.warmup)
         log(f"decode: {e * 1e3:.1f} us/step, {DN * DH * DEC_BYTES_PER_HEAD / e / 1e6:.1f} GB/s")
+        return
+    if args.only == "varlen":
+        lengths, w, e = bench_varlen(args.steps, args.warmup)
+        log(f"varlen fwd ({len(lengths)} sequences): {e * 1e3:.1f} us/step")
         return
     bwd_bytes = BB * BH_ * BT * BWD_BYTES_PER_TOKEN + BB * BH_ * BWD_STATE_BYTES_PER_HEAD
     if args.only == "bwd":
@@ -278,6 +329,12 @@ def main():
         small[f"N={n}"] = {"us_per_step": ev * 1e3,
                            "GB_per_s": n * DH * DEC_BYTES_PER_HEAD / (ev * 1e-3) / 1e9}
         log(f"decode N={n}: {ev * 1e3:.1f} us/step")
+
+    lengths, var_wall, var_ev = bench_varlen(args.steps, args.warmup)
+    var_bytes = VH * VT * FWD_BYTES_PER_TOKEN + len(lengths) * VH * FWD_STATE_BYTES_PER_HEAD
+    var_gbs = var_bytes / (var_ev * 1e-3) / 1e9
+    log(f"varlen fwd ({len(lengths)} sequences, longest {max(lengths)}): "
+        f"{var_ev * 1e3:.1f} us/step, {var_gbs:.0f} GB/s")
 
     bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
     bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
@@ -330,6 +387,18 @@ def main():
             "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
             "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
             "small_batch": {"workload": "decode H=32 d=128, N sequences (latency)", **small},
+        },
+        "varlen_fwd": {
+            "workload": (f"gdn2_chunk_fwd_varlen H={VH}, {VT} tokens per head packed as "
+                         f"{len(lengths)} documents (long-tailed lengths, mean {VMEAN}), "
+                         f"d_k=d_v=128"),
+            "lengths_min_max": [min(lengths), max(lengths)],
+            "us_per_step": var_ev * 1e3,
+            "wall_us_per_step": var_wall * 1e3,
+            "head_tokens_per_s": VH * VT / (var_wall * 1e-3),
+            "GB_per_s": var_gbs,
+            "frac_hbm_peak": var_gbs / HBM_PEAK_GBS,
+            "bytes_per_step": var_bytes,
         },
         "backward": {
             "workload": "gdn2_chunk_bwd B=1 H=32 T=16384 d_k=d_v=128 chunk=64, dO only",

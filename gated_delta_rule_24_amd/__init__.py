@@ -62,6 +62,10 @@ def _load():
         lib.gdr_chunk_fwd_workspace_bytes.restype = S
         lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 6 + [U, P, S, P]
         lib.gdr_chunk_fwd.restype = I
+        lib.gdr_chunk_fwd_varlen_workspace_bytes.argtypes = [I] * 5 + [U]
+        lib.gdr_chunk_fwd_varlen_workspace_bytes.restype = S
+        lib.gdr_chunk_fwd_varlen.argtypes = [P] * 10 + [I] * 5 + [U, P, S, P]
+        lib.gdr_chunk_fwd_varlen.restype = I
         lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 4 + [U, P]
         lib.gdr_decode_step.restype = I
         lib.gdr_chunk_bwd_workspace_bytes.argtypes = [I] * 6 + [U]
@@ -78,7 +82,7 @@ def lib():
 
 
 EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
-                    "gdr_chunk_fwd",
+                    "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
                     "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd")
 
 
@@ -139,6 +143,19 @@ def gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, B, H, T, d_k, d_v, c
     _check("gdr_chunk_fwd", st)
 
 
+def gdr_chunk_fwd_varlen_workspace_bytes(nseq, H, T, d_k, d_v, flags) -> int:
+    return int(_load().gdr_chunk_fwd_varlen_workspace_bytes(nseq, H, T, d_k, d_v, flags))
+
+
+def gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, nseq, H, T, d_k,
+                         d_v, flags, workspace, workspace_bytes, stream=None):
+    st = _load().gdr_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                      _ptr(w), _ptr(S0), _ptr(o), _ptr(S_final),
+                                      _ptr(cu_seqlens), nseq, H, T, d_k, d_v, flags,
+                                      _ptr(workspace), workspace_bytes, _stream(stream))
+    _check("gdr_chunk_fwd_varlen", st)
+
+
 def gdr_decode_step(q, k, v, log_alpha, b, w, S, o, N, H, d_k, d_v, flags, stream=None):
     st = _load().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                  _ptr(S), _ptr(o), N, H, d_k, d_v, flags, _stream(stream))
@@ -191,6 +208,30 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
         raise ValueError(f"unknown path {path!r}")
     gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, Sf, B, H, T, dk, dv, chunk, flags, ws, nbytes,
                   stream)
+    return o, Sf
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, out_dtype=torch.float32,
+                     return_state: bool = True, stream=None):
+    """Packed sequences: q, k: [H,T,dk]; v: [H,T,dv]; log_alpha, b: [H,T,dk] or
+    [H,T]; w: [H,T,dv] or [H,T]; cu_seqlens: int32 [nseq+1] on the GPU; S0:
+    [nseq,H,dk,dv] fp32 or None.  Returns (o [H,T,dv], S_final [nseq,H,dk,dv] or None)."""
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    nseq = cu_seqlens.numel() - 1
+    flags = gate_flags(q, log_alpha, b, w)
+    if out_dtype == torch.bfloat16:
+        flags |= GDR_OUT_BF16
+    o = torch.empty((H, T, dv), dtype=out_dtype, device=q.device)
+    Sf = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
+    nbytes = gdr_chunk_fwd_varlen_workspace_bytes(nseq, H, T, dk, dv, flags)
+    if nbytes == 0:
+        raise GdrError("gdr_chunk_fwd_varlen_workspace_bytes", 2)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, S0, o, Sf, cu_seqlens, nseq, H, T, dk, dv,
+                         flags, ws, nbytes, stream)
     return o, Sf
 
 

@@ -88,10 +88,48 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     gdr::FwdParams p;
     p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
     p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
+    p.cu_seqlens = nullptr; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = 0;
     p.BH = B * H; p.T = T; p.flags = flags;
     if (two_pass) return from_hip(gdr::launch_fwd_wy(p, d_k, d_v, workspace, (hipStream_t)stream));
     int used = 0;
     return from_hip(gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used));
+}
+
+size_t gdr_chunk_fwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v,
+                                            uint32_t flags) {
+    if (nseq < 1 || H < 1 || T < 0 || (long long)nseq * H > (1LL << 28)) return 0;
+    if ((flags & ~kKnownFlags) || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return 0;
+    return gdr::fwd_wy_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+}
+
+gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* b, const void* w,
+                                const float* S0, void* o, float* S_final,
+                                const int* cu_seqlens, int nseq, int H, int T,
+                                int d_k, int d_v, uint32_t flags, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (flags & ~kKnownFlags) return GDR_ERR_INVALID_ARG;
+    if (nseq < 1 || H < 1 || T < 0 || !cu_seqlens) return GDR_ERR_INVALID_ARG;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    // work items (head, chunk) are numbered in 32-bit integers
+    if ((long long)nseq * H > (1LL << 28) || (long long)H * (T / 64 + nseq) > (1LL << 30))
+        return GDR_ERR_INVALID_ARG;
+    if (!gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return GDR_ERR_UNSUPPORTED;
+    const size_t need = gdr::fwd_wy_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+
+    gdr::FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
+    p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
+    p.cu_seqlens = cu_seqlens; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = nseq;
+    p.BH = H; p.T = T; p.flags = flags;
+    return from_hip(gdr::launch_fwd_wy_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -936,6 +936,7 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
     FwdParams f;
     f.q = p.q; f.k = p.k; f.v = p.v; f.la = p.la; f.b = p.b; f.w = p.w; f.S0 = p.S0;
     f.o = nullptr; f.Sf = nullptr; f.states = nullptr; f.state_frags = nullptr;
+    f.cu_seqlens = nullptr; f.chunk_off = nullptr; f.chunk_tab = nullptr; f.seq_order = nullptr; f.nseq = 0;
     f.BH = p.BH; f.T = p.T; f.flags = p.flags & ~(uint32_t)GDR_OUT_BF16;
     hipError_t e;
     if (bwd_two_pass(dk, dv, p.T, cb, p.flags)) {

@@ -67,7 +67,25 @@ struct PrepLayout {
     static constexpr size_t bytes = oFl + (size_t)(NT / 64) * 4;
 };
 
-template <int DK, int DV, bool AS, bool BS, bool WS, bool BL>
+// The chunk of work item idx (CN chunks per head): its first token in the
+// activation streams and its number of tokens.  Fixed length: item =
+// (sequence, chunk).  Packed sequences (VL): item = (head, chunk r of the
+// head's concatenated sequences), looked up in the chunk table; a sequence's
+// last chunk may be partial.
+template <bool VL>
+__device__ __forceinline__ void chunk_item(const FwdParams& p, int CN, int idx, size_t& tok0, int& len) {
+    const int h = idx / CN, r = idx - h * CN;
+    if constexpr (VL) {
+        const int2 e = reinterpret_cast<const int2*>(p.chunk_tab)[r];
+        tok0 = (size_t)h * p.T + (size_t)e.x;
+        len = e.y;
+    } else {
+        tok0 = (size_t)h * p.T + (size_t)r * C;
+        len = C;
+    }
+}
+
+template <int DK, int DV, bool AS, bool BS, bool WS, bool BL, bool VL>
 __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdParams p, unsigned char* ws) {
     using L = PrepLayout<DK, DV>;
     constexpr int NT = L::NT, NW = NT / 64;
@@ -99,8 +117,8 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     const int r16 = lane & 15, g4 = 4 * (lane >> 4);
     const int co = tid % CO, part = tid / CO;       // channels 8co.., tokens part*TPP..
     const int vo = tid % VO, xpart = tid / VO;      // columns 8vo.., tokens xpart*XTP..
-    const int NC = p.T / C;
-    const int total = p.BH * NC;
+    const int CN = VL ? p.chunk_off[p.nseq] : p.T / C;      // chunks per head
+    const int total = p.BH * CN;
     const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b);
     const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v);
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(p.w);
@@ -122,17 +140,22 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     // The loads of a chunk are issued in three groups spread over the previous
     // chunk's phases (q and k, then b and log alpha, then v and w), so that
     // their transfer overlaps computation instead of stalling one issue point.
-    auto issue = [&](int idx, int group) __attribute__((always_inline)) {
-        const int bh = idx / NC, c = idx % NC;
-        const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+    // (packed sequences: the tokens past a sequence's end in its last chunk read
+    // as zeros, log alpha 0 included, so they leave the state unchanged; the
+    // loads themselves go to the chunk's first token)
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    auto issue = [&](size_t tok0, int len, int group) __attribute__((always_inline)) {
         if (group < 2) {
 #pragma unroll
             for (int j = 0; j < TPP; ++j) {
-                const size_t t = tok0 + part * TPP + j;
+                const int row = part * TPP + j;
+                const bool ok = !VL || row < len;
+                const size_t t = tok0 + (ok ? row : 0);
                 const size_t ix = t * DK + 8 * co;
                 if (group == 0) {
                     rq[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + ix);
                     rk[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + ix);
+                    if (!ok) rq[j] = rk[j] = z4;
                 } else {
                     if constexpr (BS) rb[j][0] = bg[t];
                     else rb[j] = *reinterpret_cast<const u32x4*>(bg + ix);
@@ -142,16 +165,23 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                         rla[j][0] = *reinterpret_cast<const floatx4*>(p.la + ix);
                         rla[j][1] = *reinterpret_cast<const floatx4*>(p.la + ix + 4);
                     }
+                    if (!ok) {
+                        rb[j] = z4;
+                        rla[j][0] = rla[j][1] = zero4();
+                    }
                 }
             }
         } else {
 #pragma unroll
             for (int j = 0; j < XTP; ++j) {
-                const size_t t = tok0 + xpart * XTP + j;
+                const int row = xpart * XTP + j;
+                const bool ok = !VL || row < len;
+                const size_t t = tok0 + (ok ? row : 0);
                 const size_t ix = t * DV + 8 * vo;
                 rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
                 if constexpr (WS) rw[j][0] = wg[t];
                 else rw[j] = *reinterpret_cast<const u32x4*>(wg + ix);
+                if (!ok) rv[j] = rw[j] = z4;
             }
         }
     };
@@ -165,12 +195,19 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
 
     int idx = blockIdx.x;
     if (idx < total) {
-        issue(idx, 0);
-        issue(idx, 1);
-        issue(idx, 2);
+        size_t tok0;
+        int len;
+        chunk_item<VL>(p, CN, idx, tok0, len);
+        issue(tok0, len, 0);
+        issue(tok0, len, 1);
+        issue(tok0, len, 2);
     }
     for (; idx < total; idx += gridDim.x) {
         const int nx = idx + (int)gridDim.x < total ? idx + (int)gridDim.x : idx;
+        // the next item's chunk (its table entry loads while this one is processed)
+        size_t ntok0;
+        int nlen;
+        chunk_item<VL>(p, CN, nx, ntok0, nlen);
         constexpr size_t RB = BL ? R::bwd_bytes : R::bytes;
         unsigned char* rec = ws + (size_t)idx * RB;
         // ---------------- element-wise: in-chunk prefix, E, Qs, Kh, X (fp32 -> f16)
@@ -309,7 +346,7 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
         }
         if (tid == 0) *reinterpret_cast<int*>(rec + R::G + DK * 4) = over;
         // the next chunk's inputs load while this one is processed
-        issue(nx, 0);
+        issue(ntok0, nlen, 0);
 
         // ---------------- A = strict_lower(E Kh^T) (fp32), P = lower(Qs Kh^T) (f16)
         // One lower tile (mt, nt) per task gives both its A and its P tile: the
@@ -359,7 +396,7 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
             }
         }
         lds_barrier();
-        issue(nx, 1);
+        issue(ntok0, nlen, 1);
         if (wave == 0) {
             // diagonal 16x16 blocks of T: right-looking forward substitution in fp32,
             // lane (blk, column jc), the columns of A streamed from the transposed copy
@@ -485,7 +522,7 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 cat8(to_h4(acc[0]), to_h4(acc[1])));
         }
         lds_barrier();
-        issue(nx, 2);
+        issue(ntok0, nlen, 2);
         // ---------------- Q̃^T = Qs^T - W^T P^T (fragments of Q̃ out); P's upper tiles are zero
 #pragma unroll
         for (int s2 = 0; s2 < NB * NKK / (NT / 64); ++s2) {
@@ -580,7 +617,7 @@ struct OutFrags {
     int flag;
 };
 
-template <int DK, int DV, int NS>
+template <int DK, int DV, int NS, bool VL>
 __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsigned char* ws, size_t RB) {
     using R = Rec<DK, DV>;
     constexpr int NGRP = DV / (16 * NS), NKT = DK / 16, NKK = DK / 32, NB = C / 16, NK2 = C / 32;
@@ -589,10 +626,45 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     __shared__ __align__(16) float sO[C * LDO];         // output wave only: O tile, row-major
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = lid / NGRP, ng = lid % NGRP;          // strips NS*ng .. NS*ng+NS-1
-    const int NC = p.T / C;
-    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
+    // chain bh: a (batch, head) sequence, or for packed sequences sequence
+    // bh / H of head bh % H (its state is S0[bh], as [nseq, H] is laid out)
+    int bh, ng;                                          // strips NS*ng .. NS*ng+NS-1
+    if constexpr (VL) {
+        // packed sequences: chains of very different lengths.  The longest go
+        // first (seq_order), dealt round-robin over the XCDs (workgroup b runs
+        // on XCD b % 8) with the strips of one chain kept on one XCD.
+        const int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+        int rank;
+        if (nblk % (8 * NGRP) == 0) {
+            const int pos = bid / 8;
+            rank = (pos / NGRP) * 8 + bid % 8;
+            ng = pos % NGRP;
+        } else {
+            rank = bid / NGRP;
+            ng = bid % NGRP;
+        }
+        bh = p.seq_order[rank / p.BH] * p.BH + rank % p.BH;
+    } else {
+        const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        bh = lid / NGRP;
+        ng = lid % NGRP;
+    }
+    int NC, seq_len;
+    size_t tok_base;                                     // the chain's first token
+    const unsigned char* rec0;
+    if constexpr (VL) {
+        const int s = bh / p.BH, h = bh % p.BH;
+        const int c0 = p.chunk_off[s];
+        NC = p.chunk_off[s + 1] - c0;
+        seq_len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
+        tok_base = (size_t)h * p.T + (size_t)p.cu_seqlens[s];
+        rec0 = ws + ((size_t)h * p.chunk_off[p.nseq] + c0) * RB;
+    } else {
+        NC = p.T / C;
+        seq_len = p.T;
+        tok_base = (size_t)bh * p.T;
+        rec0 = ws + (size_t)bh * NC * RB;
+    }
     const int n_l = lane & 15, g4 = 4 * (lane >> 4);
     auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
         return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
@@ -711,11 +783,12 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
                 for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sO[(16 * rt + g4 + i) * LDO + 16 * s + n_l] = O[s][rt][i];
-            const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+            const size_t tok0 = tok_base + (size_t)c * C;
             constexpr int QPR = 4 * NS;                      // column quads per row
 #pragma unroll
             for (int r = 0; r < C * QPR / 64; ++r) {
                 const int e = lane + 64 * r, row = e / QPR, cq = e % QPR;
+                if (VL && c * C + row >= seq_len) continue;  // past the sequence's end
                 floatx4 o = *reinterpret_cast<const floatx4*>(sO + row * LDO + 4 * cq);
                 if (poisoned) o = o * __builtin_nanf("");
                 const size_t base = (tok0 + row) * DV + 16 * NS * ng + 4 * cq;
@@ -864,11 +937,11 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
 
 constexpr int kChainStrips = 1;
 
-template <int DK, int DV, bool AS, bool BS, bool WS, bool BL>
+template <int DK, int DV, bool AS, bool BS, bool WS, bool BL, bool VL>
 static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int passes) {
     using LP = PrepLayout<DK, DV>;
-    auto kp = wy_kernel<DK, DV, AS, BS, WS, BL>;
-    auto ks = chain_kernel<DK, DV, kChainStrips>;
+    auto kp = wy_kernel<DK, DV, AS, BS, WS, BL, VL>;
+    auto ks = chain_kernel<DK, DV, kChainStrips, VL>;
     constexpr size_t RB = BL ? Rec<DK, DV>::bwd_bytes : Rec<DK, DV>::bytes;
     static bool attr_done = false;
     if (!attr_done) {
@@ -877,7 +950,9 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int pas
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    const int total = p.BH * (p.T / C);
+    // (packed sequences: the chunk count is on the device; the WY grid is one
+    // workgroup per compute unit)
+    const int total = VL ? 1 << 30 : p.BH * (p.T / C);
     int ncu = 256;
     {
         int dev = 0;
@@ -895,27 +970,96 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int pas
         if (e != hipSuccess) return e;
     }
     if (passes & kChainPass) {
-        hipLaunchKernelGGL(ks, dim3((unsigned)(p.BH * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
+        const int chains = VL ? p.nseq * p.BH : p.BH;
+        hipLaunchKernelGGL(ks, dim3((unsigned)(chains * (DV / (16 * kChainStrips)))), dim3(128), 0, st, p,
                            reinterpret_cast<const unsigned char*>(ws), RB);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
-template <int DK, int DV, bool BL>
+template <int DK, int DV, bool BL, bool VL = false>
 static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st, int passes) {
     const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
     const int m = (as ? 4 : 0) | (bs ? 2 : 0) | (wsc ? 1 : 0);
     switch (m) {
-        case 0: return launch_t<DK, DV, false, false, false, BL>(p, ws, st, passes);
-        case 1: return launch_t<DK, DV, false, false, true, BL>(p, ws, st, passes);
-        case 2: return launch_t<DK, DV, false, true, false, BL>(p, ws, st, passes);
-        case 3: return launch_t<DK, DV, false, true, true, BL>(p, ws, st, passes);
-        case 4: return launch_t<DK, DV, true, false, false, BL>(p, ws, st, passes);
-        case 5: return launch_t<DK, DV, true, false, true, BL>(p, ws, st, passes);
-        case 6: return launch_t<DK, DV, true, true, false, BL>(p, ws, st, passes);
-        default: return launch_t<DK, DV, true, true, true, BL>(p, ws, st, passes);
+        case 0: return launch_t<DK, DV, false, false, false, BL, VL>(p, ws, st, passes);
+        case 1: return launch_t<DK, DV, false, false, true, BL, VL>(p, ws, st, passes);
+        case 2: return launch_t<DK, DV, false, true, false, BL, VL>(p, ws, st, passes);
+        case 3: return launch_t<DK, DV, false, true, true, BL, VL>(p, ws, st, passes);
+        case 4: return launch_t<DK, DV, true, false, false, BL, VL>(p, ws, st, passes);
+        case 5: return launch_t<DK, DV, true, false, true, BL, VL>(p, ws, st, passes);
+        case 6: return launch_t<DK, DV, true, true, false, BL, VL>(p, ws, st, passes);
+        default: return launch_t<DK, DV, true, true, true, BL, VL>(p, ws, st, passes);
     }
+}
+
+// chunk_off[s] = number of chunks of the packed sequences before s (each
+// sequence's last chunk may be partial), chunk_off[nseq] their total; one
+// workgroup: contiguous runs of sequences per thread, then a scan of the runs.
+// Also order[]: the sequences by descending class floor(log2(chunks)) + 1
+// (class 0: empty), any order within a class (the chains are independent, so
+// the order changes only which workgroup runs which chain).
+__global__ __launch_bounds__(1024) void varlen_chunk_offsets(const int* cu, int n, int* off, int* order) {
+    __shared__ int part[1024];
+    __shared__ int cls_n[33], cls_fill[33];
+    if (threadIdx.x < 33) cls_n[threadIdx.x] = cls_fill[threadIdx.x] = 0;
+    const int t = threadIdx.x;
+    const int per = (n + 1023) / 1024;
+    const int s0 = min(n, t * per), s1 = min(n, s0 + per);
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) sum += (cu[s + 1] - cu[s] + C - 1) / C;
+    part[t] = sum;
+    __syncthreads();
+    for (int d = 1; d < 1024; d *= 2) {
+        const int v = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int run = t ? part[t - 1] : 0;
+    for (int s = s0; s < s1; ++s) {
+        off[s] = run;
+        run += (cu[s + 1] - cu[s] + C - 1) / C;
+    }
+    if (t == 1023) off[n] = part[1023];
+    // longest-first order by class: count, start of each class, then place
+    for (int s = s0; s < s1; ++s) {
+        const int nc = (cu[s + 1] - cu[s] + C - 1) / C;
+        atomicAdd(&cls_n[nc ? 32 - __clz(nc) : 0], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int c = 32; c >= 0; --c) {
+            const int k = cls_n[c];
+            cls_n[c] = run;
+            run += k;
+        }
+    }
+    __syncthreads();
+    for (int s = s0; s < s1; ++s) {
+        const int nc = (cu[s + 1] - cu[s] + C - 1) / C;
+        const int c = nc ? 32 - __clz(nc) : 0;
+        order[cls_n[c] + atomicAdd(&cls_fill[c], 1)] = s;
+    }
+}
+
+// chunk_tab[r] = (first token, token count) of chunk r of the packed sequences
+// (r < chunk_off[n]; the grid covers the largest possible chunk count)
+__global__ __launch_bounds__(256) void varlen_chunk_table(const int* cu, const int* off, int n,
+                                                          int max_chunks, int* tab) {
+    const int r = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (r >= max_chunks || r >= off[n]) return;
+    int lo = 0, hi = n;                               // off[lo] <= r < off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid;
+        else hi = mid;
+    }
+    const int start = cu[lo] + (r - off[lo]) * C;
+    tab[2 * r] = start;
+    tab[2 * r + 1] = min(C, cu[lo + 1] - start);
 }
 
 }  // namespace wy
@@ -950,5 +1094,53 @@ hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream
     return hipErrorInvalidValue;
 }
 
+
+static size_t varlen_rec_bytes(int dk, int dv) {
+    if (dk == 128 && dv == 128) return wy::Rec<128, 128>::bytes;
+    if (dk == 64 && dv == 64) return wy::Rec<64, 64>::bytes;
+    if (dk == 128 && dv == 64) return wy::Rec<128, 64>::bytes;
+    if (dk == 64 && dv == 128) return wy::Rec<64, 128>::bytes;
+    return 0;
+}
+
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv) {
+    const size_t rb = varlen_rec_bytes(dk, dv);
+    if (rb == 0 || H < 1 || nseq < 1 || T < 0) return 0;
+    // every sequence has at most len / C + 1 chunks
+    const size_t max_chunks = (size_t)(T / wy::C) + (size_t)nseq;
+    return (size_t)H * max_chunks * rb + round256(((size_t)nseq + 1) * sizeof(int)) +
+           round256(max_chunks * 2 * sizeof(int)) + round256((size_t)nseq * sizeof(int));
+}
+
+hipError_t launch_fwd_wy_varlen(const FwdParams& p0, int dk, int dv, void* ws, size_t ws_bytes,
+                                hipStream_t st) {
+    const size_t need = fwd_wy_varlen_workspace_bytes(p0.BH, p0.T, p0.nseq, dk, dv);
+    if (need == 0 || ws_bytes < need || !p0.cu_seqlens) return hipErrorInvalidValue;
+    FwdParams p = p0;
+    const size_t rb = varlen_rec_bytes(dk, dv);
+    const size_t max_chunks = (size_t)(p.T / wy::C) + (size_t)p.nseq;
+    unsigned char* tail = reinterpret_cast<unsigned char*>(ws) + (size_t)p.BH * max_chunks * rb;
+    p.chunk_off = reinterpret_cast<int*>(tail);
+    tail += round256(((size_t)p.nseq + 1) * sizeof(int));
+    p.chunk_tab = reinterpret_cast<int*>(tail);
+    tail += round256(max_chunks * 2 * sizeof(int));
+    p.seq_order = reinterpret_cast<int*>(tail);
+    hipLaunchKernelGGL(wy::varlen_chunk_offsets, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.nseq, p.chunk_off,
+                       p.seq_order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wy::varlen_chunk_table, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, st,
+                       p.cu_seqlens, p.chunk_off, p.nseq, (int)max_chunks, p.chunk_tab);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int passes = kWyPass | kChainPass;
+    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false, true>(p, ws, st, passes);
+    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false, true>(p, ws, st, passes);
+    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false, true>(p, ws, st, passes);
+    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false, true>(p, ws, st, passes);
+    return hipErrorInvalidValue;
+}
 
 }  // namespace gdr

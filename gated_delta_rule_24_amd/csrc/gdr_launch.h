@@ -37,9 +37,15 @@ struct FwdParams {
                            // generic forward)
     void* state_frags;     // optional: decayed chunk-start states S' as f16 fragments
                            // (backward recompute, two-pass forward; wy::StateFrag layout)
-    int BH;
-    int T;
+    int BH;                // fixed length: B*H sequences of T tokens each
+    int T;                 // packed (cu_seqlens set): BH = H heads, T = total tokens per head
     uint32_t flags;
+    // packed variable-length sequences (two-pass forward only), or null:
+    const int* cu_seqlens; // [nseq + 1] token offsets of the sequences within each head
+    int* chunk_off;        // [nseq + 1] offsets of their chunks (filled on the device)
+    int* chunk_tab;        // [chunks][2] first token and token count of each chunk (device)
+    int* seq_order;        // [nseq] sequences, longest first by power-of-two chunk-count class
+    int nseq;
 };
 
 hipError_t launch_decode(const DecodeParams& p, int dk, int dv, hipStream_t st);
@@ -64,6 +70,12 @@ size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts = 
 constexpr int kWyPass = 1, kChainPass = 2;
 hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st,
                          bool bwd_layouts = false, int passes = kWyPass | kChainPass);
+// Packed variable-length sequences: workspace bytes (records of at most
+// T/64 + nseq chunks per head, then the chunk offsets and the chunk table), and
+// the two passes.
+size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
+hipError_t launch_fwd_wy_varlen(const FwdParams& p, int dk, int dv, void* ws, size_t ws_bytes,
+                                hipStream_t st);
 
 struct BwdParams {
     const void* q;

@@ -174,6 +174,31 @@ def preset(name: str, seed: int = 0, **over) -> Inputs:
     return inp
 
 
+def packed_inputs(lengths, H: int, dk: int, dv: int, seed: int = 0,
+                  s0_std: Optional[float] = 0.02, **kw) -> Inputs:
+    """Packed variable-length sequences: one stream of sum(lengths) tokens per
+    head (arrays [1, H, T, ...], the tokens drawn as by make_inputs), S0 of
+    shape [nseq, H, dk, dv] from its own stream, and arrays["cu_seqlens"]
+    (int32 [nseq + 1], the running sum of the lengths)."""
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    inp = make_inputs(1, H, T, dk, dv, seed=seed, s0_std=None, **kw)
+    nseq = len(lengths)
+    if s0_std is not None:
+        rng = np.random.default_rng([seed, 7])
+        inp.arrays["S0"] = rng.standard_normal((nseq, H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    inp.arrays["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    inp.recipe = f"packed {nseq} sequences"
+    return inp
+
+
+def packed_lengths(n: int, mean: int, seed: int = 0, lo: int = 1) -> list:
+    """n sequence lengths with a long-tailed mix (geometric around mean,
+    at least lo), as packed training batches of documents have."""
+    rng = np.random.default_rng([seed, 11])
+    return [int(max(lo, x)) for x in rng.geometric(1.0 / max(mean, 1), size=n)]
+
+
 # decode workload: 256 sequences x 32 heads, d=128, fp32 state from N(0, 0.02)
 DECODE = dict(N=256, H=32, dk=128, dv=128)
 

@@ -123,6 +123,43 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * The same forward over packed variable-length sequences: nseq sequences of
+ * any lengths stored back to back (variable-length batches are the practical
+ * extension the pages point to: "Gated DeltaNet study notes" §4-3).  Each
+ * sequence runs its own recurrence from its own initial state; no state
+ * crosses from one sequence to the next.
+ *
+ *   q, k       : act  [H, T, d_k]   (T = total tokens of all sequences)
+ *   v          : act  [H, T, d_v]
+ *   log_alpha  : fp32 [H, T, d_k]   or [H, T] with GDR_ALPHA_SCALAR
+ *   b          : act  [H, T, d_k]   or [H, T] with GDR_B_SCALAR
+ *   w          : act  [H, T, d_v]   or [H, T] with GDR_W_SCALAR
+ *   cu_seqlens : int32 [nseq + 1], DEVICE memory: sequence s is tokens
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1 of every head.  The
+ *                caller guarantees cu_seqlens[0] = 0, non-decreasing values
+ *                and cu_seqlens[nseq] = T (the library cannot check values in
+ *                device memory).  Lengths need not be multiples of 64; a
+ *                length of 0 copies that sequence's S0 to S_final.
+ *   S0         : fp32 [nseq, H, d_k, d_v]; NULL means zeros
+ *   o          : as gdr_chunk_fwd, [H, T, d_v]
+ *   S_final    : fp32 [nseq, H, d_k, d_v]; NULL means not written; may alias S0
+ *   workspace  : required, at least gdr_chunk_fwd_varlen_workspace_bytes()
+ *                bytes (the two-pass path with chunks of 64; the tokens past a
+ *                sequence's end in its last chunk are treated as absent).
+ * Supported: bf16 activations, d_k and d_v in {64, 128}; nseq >= 1, H >= 1,
+ * T >= 0.  Returns GDR_ERR_UNSUPPORTED otherwise.
+ */
+size_t gdr_chunk_fwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v,
+                                            uint32_t flags);
+
+gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* b, const void* w,
+                                const float* S0, void* o, float* S_final,
+                                const int* cu_seqlens, int nseq, int H, int T,
+                                int d_k, int d_v, uint32_t flags, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for N independent sequences (constant memory:
  * the state is updated in place; Q&A page introduction, "Gated DeltaNet-2
  * Review" §3-2 item 1).  Each (n, h) state is read once and written once.

@@ -130,3 +130,40 @@ def test_bwd_workspace_query_and_validation():
     assert call(ws=MIS) == 1
     assert call(dk=32, dv=32) == 2
     assert call(chunk=16) == 2
+
+
+def _fwd_varlen(lib, **kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, Sf=None, cu=A, nseq=2, H=1, T=100,
+                dk=128, dv=128, flags=0, ws=A, nbytes=1 << 30)
+    args.update(kw)
+    return lib.gdr_chunk_fwd_varlen(args["q"], args["k"], args["v"], args["la"], args["b"],
+                                    args["w"], args["S0"], args["o"], args["Sf"], args["cu"],
+                                    args["nseq"], args["H"], args["T"], args["dk"], args["dv"],
+                                    args["flags"], args["ws"], args["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(cu=None), 1), (dict(nseq=0), 1),
+    (dict(H=0), 1), (dict(T=-1), 1), (dict(flags=0x100), 1), (dict(v=MIS), 1),
+    (dict(S0=MIS), 1), (dict(ws=MIS), 1), (dict(ws=None), 3), (dict(nbytes=1024), 3),
+    (dict(H=1 << 20, T=1 << 20), 1),
+    (dict(dk=32, dv=32), 2), (dict(dk=96), 2), (dict(flags=0x1), 2), (dict(flags=0x20), 2),
+])
+def test_fwd_varlen_argument_validation(kw, status):
+    assert _fwd_varlen(_lib(), **kw) == status
+
+
+def test_fwd_varlen_workspace_query():
+    lib = _lib()
+    # one record per chunk: a sequence of n tokens has ceil(n/64) <= n//64 + 1 chunks,
+    # so H * (T//64 + nseq) records cover any split of T tokens into nseq sequences;
+    # then the nseq+1 chunk offsets, the (T//64 + nseq) x 2 chunk table and the
+    # nseq-long sequence order (int32), each rounded up to 256 bytes
+    rec = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0)
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(3, 2, 200, 128, 128, 0) == 2 * (3 + 3) * rec + 768
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(64, 1, 0, 128, 128, 0) == 64 * rec + 1280
+    rec64 = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0)
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 4, 128, 64, 64, 0x1c) == 4 * 3 * rec64 + 768
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0   # fp32
+    assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 32, 32, 0) == 0
