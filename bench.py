@@ -218,6 +218,37 @@ def bench_varlen(steps, warmup):
     return lengths, wall_ms, ev_ms
 
 
+def bench_bwd_varlen(steps, warmup):
+    """The backward workload's 32 heads x 16384 tokens packed as documents of
+    the lengths varlen_lengths() gives."""
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    lengths = varlen_lengths()
+    inp = gs.packed_inputs(lengths, BH_, FD, FD, seed=0, with_dO=True)
+    a = inp.arrays
+    d = {n: torch.from_numpy(np.ascontiguousarray(a[n][0])).to(
+        torch.float32 if n == "log_alpha" else torch.bfloat16).cuda()
+        for n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+    S0 = torch.from_numpy(a["S0"]).cuda()
+    cu = torch.from_numpy(a["cu_seqlens"]).cuda()
+    nseq = len(lengths)
+    f32 = torch.float32
+    g = {n: torch.empty((BH_, VT, FD), dtype=f32, device="cuda")
+         for n in ("dq", "dk", "dv", "dla", "db", "dw")}
+    dS0 = torch.empty((nseq, BH_, FD, FD), dtype=f32, device="cuda")
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    nbytes = gdr.gdr_chunk_bwd_varlen_workspace_bytes(nseq, BH_, VT, FD, FD, flags)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdr.gdr_chunk_bwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0,
+                                 d["dO"], None, g["dq"], g["dk"], g["dv"], g["dla"], g["db"],
+                                 g["dw"], dS0, cu, nseq, BH_, VT, FD, FD, flags, ws, nbytes)
+    wall_ms, ev_ms = time_loop(step, steps, warmup)
+    return lengths, wall_ms, ev_ms
+
+
 def bench_copy(steps, warmup):
     """Plain 1 GiB device copy, the calibration kernel for HBM counters."""
     import torch
@@ -276,7 +307,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen", "bwd_varlen"],
+                    default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -309,6 +341,10 @@ def main():
         w, e, _ = bench_bwd(args.steps, args.warmup)
         log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
         return
+    if args.only == "bwd_varlen":
+        lengths, w, e = bench_bwd_varlen(args.steps, args.warmup)
+        log(f"bwd varlen ({len(lengths)} sequences): {e * 1e3:.1f} us/step")
+        return
 
     inp, wall_ms, ev_ms = bench_fwd(args.steps, args.warmup)
     ntok = FB * FH * FT
@@ -339,6 +375,10 @@ def main():
     bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
     bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
     log(f"bwd: {bwd_ev * 1e3:.1f} us/step, {bwd_gbs:.0f} GB/s")
+
+    _, bv_wall, bv_ev = bench_bwd_varlen(max(3, args.steps // 4), min(args.warmup, 2))
+    bv_bytes = BH_ * VT * BWD_BYTES_PER_TOKEN + len(lengths) * BH_ * BWD_STATE_BYTES_PER_HEAD
+    log(f"bwd varlen: {bv_ev * 1e3:.1f} us/step, {bv_bytes / (bv_ev * 1e-3) / 1e9:.0f} GB/s")
 
     traffic = measured_traffic()
     result = {
@@ -408,6 +448,15 @@ def main():
             "frac_hbm_peak": bwd_gbs / HBM_PEAK_GBS,
             "bytes_per_step": bwd_bytes,
             "workspace_bytes": bwd_ws,
+        },
+        "varlen_bwd": {
+            "workload": (f"gdn2_chunk_bwd_varlen H={BH_}, {VT} tokens per head packed as "
+                         f"{len(lengths)} documents (the varlen_fwd lengths), d_k=d_v=128, dO only"),
+            "us_per_step": bv_ev * 1e3,
+            "head_tokens_per_s": BH_ * VT / (bv_wall * 1e-3),
+            "GB_per_s": bv_bytes / (bv_ev * 1e-3) / 1e9,
+            "frac_hbm_peak": bv_bytes / (bv_ev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": bv_bytes,
         },
     }
     if not args.no_cpu_baseline:

@@ -6,14 +6,17 @@ used only for device memory and the current stream.  There is no CPU or
 PyTorch fallback: if the library is missing or the device is not a gfx950,
 calls raise.
 
-The three entry points keep the C names:
+The entry points keep the C names:
 
 * :func:`gdr_chunk_fwd`   — chunkwise-parallel forward
 * :func:`gdr_decode_step` — one recurrent decode step, state updated in place
 * :func:`gdr_chunk_bwd`   — gate-aware backward
+* :func:`gdr_chunk_fwd_varlen`, :func:`gdr_chunk_bwd_varlen` — the forward
+  and backward over packed variable-length sequences
 
-and :func:`chunk_fwd`, :func:`decode_step`, :func:`chunk_bwd` are the same
-calls with outputs allocated for the caller.
+and :func:`chunk_fwd`, :func:`decode_step`, :func:`chunk_bwd`,
+:func:`chunk_fwd_varlen`, :func:`chunk_bwd_varlen` are the same calls with
+outputs allocated for the caller.
 """
 from __future__ import annotations
 
@@ -72,6 +75,10 @@ def _load():
         lib.gdr_chunk_bwd_workspace_bytes.restype = S
         lib.gdr_chunk_bwd.argtypes = [P] * 16 + [I] * 6 + [U, P, S, P]
         lib.gdr_chunk_bwd.restype = I
+        lib.gdr_chunk_bwd_varlen_workspace_bytes.argtypes = [I] * 5 + [U]
+        lib.gdr_chunk_bwd_varlen_workspace_bytes.restype = S
+        lib.gdr_chunk_bwd_varlen.argtypes = [P] * 17 + [I] * 5 + [U, P, S, P]
+        lib.gdr_chunk_bwd_varlen.restype = I
         _lib = lib
     return _lib
 
@@ -83,7 +90,8 @@ def lib():
 
 EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
                     "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
-                    "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd")
+                    "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
+                    "gdr_chunk_bwd_varlen_workspace_bytes", "gdr_chunk_bwd_varlen")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -175,6 +183,21 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_a
                                d_v, chunk, flags, _ptr(workspace), workspace_bytes,
                                _stream(stream))
     _check("gdr_chunk_bwd", st)
+
+
+def gdr_chunk_bwd_varlen_workspace_bytes(nseq, H, T, d_k, d_v, flags) -> int:
+    return int(_load().gdr_chunk_bwd_varlen_workspace_bytes(nseq, H, T, d_k, d_v, flags))
+
+
+def gdr_chunk_bwd_varlen(q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_alpha, db,
+                         dw, dS0, cu_seqlens, nseq, H, T, d_k, d_v, flags, workspace,
+                         workspace_bytes, stream=None):
+    st = _load().gdr_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                      _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(dlog_alpha), _ptr(db), _ptr(dw),
+                                      _ptr(dS0), _ptr(cu_seqlens), nseq, H, T, d_k, d_v, flags,
+                                      _ptr(workspace), workspace_bytes, _stream(stream))
+    _check("gdr_chunk_bwd_varlen", st)
 
 
 # ---------------------------------------------------------------------------
@@ -270,4 +293,33 @@ def chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, chunk: int = 64, 
     gdr_chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final, out["dq"], out["dk"], out["dv"],
                   out["dlog_alpha"], out["db"], out["dw"], out["dS0"], B, H, T, dk, dv, chunk,
                   flags, ws, nbytes, stream)
+    return out
+
+
+def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None, stream=None):
+    """Packed sequences ([H,T,...] streams, cu_seqlens int32 on the GPU): the
+    gradients of L = <dO, o> + <dS_final, S_final> as a dict of fp32 tensors
+    dq, dk, dv, dlog_alpha, db, dw (in the inputs' shapes) and dS0 [nseq,H,dk,dv]."""
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    nseq = cu_seqlens.numel() - 1
+    flags = gate_flags(q, log_alpha, b, w)
+    dev = q.device
+    f32 = torch.float32
+    out = dict(dq=torch.empty((H, T, dk), dtype=f32, device=dev),
+               dk=torch.empty((H, T, dk), dtype=f32, device=dev),
+               dv=torch.empty((H, T, dv), dtype=f32, device=dev),
+               dlog_alpha=torch.empty(tuple(log_alpha.shape), dtype=f32, device=dev),
+               db=torch.empty(tuple(b.shape), dtype=f32, device=dev),
+               dw=torch.empty(tuple(w.shape), dtype=f32, device=dev),
+               dS0=torch.empty((nseq, H, dk, dv), dtype=f32, device=dev))
+    nbytes = gdr_chunk_bwd_varlen_workspace_bytes(nseq, H, T, dk, dv, flags)
+    if nbytes == 0:
+        raise GdrError("gdr_chunk_bwd_varlen_workspace_bytes", 2)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    gdr_chunk_bwd_varlen(q, k, v, log_alpha, b, w, S0, dO, dS_final, out["dq"], out["dk"],
+                         out["dv"], out["dlog_alpha"], out["db"], out["dw"], out["dS0"],
+                         cu_seqlens, nseq, H, T, dk, dv, flags, ws, nbytes, stream)
     return out

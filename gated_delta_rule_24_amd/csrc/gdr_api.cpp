@@ -189,6 +189,7 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
     p.dq = dq; p.dk = dk; p.dv = dv; p.dla = dlog_alpha; p.db = db; p.dw = dw; p.dS0 = dS0;
     p.states = nullptr; p.dstates = nullptr; p.records = nullptr;
     p.state_frags = nullptr; p.dstate_frags = nullptr;
+    p.cu_seqlens = nullptr; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = 0;
     p.BH = B * H; p.T = T; p.flags = flags;
     if (need > 0) {
         const size_t sb = gdr::bwd_states_bytes(B * H, T, d_k, d_v, chunk, flags);
@@ -202,6 +203,49 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
         if (need > 2 * sb) p.records = base + 2 * sb;
     }
     return from_hip(gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream));
+}
+
+size_t gdr_chunk_bwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v, uint32_t flags) {
+    if (nseq < 1 || H < 1 || T < 0 || (long long)nseq * H > (1LL << 28)) return 0;
+    if ((flags & ~(kKnownFlags & ~GDR_OUT_BF16)) || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return 0;
+    return gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+}
+
+gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const void* b, const void* w, const float* S0, const void* dO,
+                                const float* dS_final, float* dq, float* dk, float* dv,
+                                float* dlog_alpha, float* db, float* dw, float* dS0,
+                                const int* cu_seqlens, int nseq, int H, int T, int d_k, int d_v,
+                                uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    if (flags & ~(kKnownFlags & ~GDR_OUT_BF16)) return GDR_ERR_INVALID_ARG;
+    if (nseq < 1 || H < 1 || T < 0 || !cu_seqlens) return GDR_ERR_INVALID_ARG;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv ||
+                  !dlog_alpha || !db || !dw))
+        return GDR_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv,
+                          dlog_alpha, db, dw, dS0, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    // work items (head, chunk) are numbered in 32-bit integers
+    if ((long long)nseq * H > (1LL << 28) || (long long)H * (T / 64 + nseq) > (1LL << 30))
+        return GDR_ERR_INVALID_ARG;
+    if (d_k != d_v || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return GDR_ERR_UNSUPPORTED;
+    const size_t need = gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+
+    gdr::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w; p.S0 = S0;
+    p.dO = dO; p.dSf = dS_final;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dla = dlog_alpha; p.db = db; p.dw = dw; p.dS0 = dS0;
+    p.states = nullptr; p.dstates = nullptr; p.records = nullptr;
+    p.state_frags = nullptr; p.dstate_frags = nullptr;
+    p.cu_seqlens = cu_seqlens; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr;
+    p.nseq = nseq;
+    p.BH = H; p.T = T; p.flags = flags;
+    return from_hip(gdr::launch_bwd_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -900,6 +900,40 @@ hipError_t side_init(SideStream& sd) {
 }
 }  // namespace
 
+// The two chains of the two-pass backward: the reverse chain (dchain) on the
+// side stream, forked from and joined back to st, beside the forward state
+// chain (state_chain) on st; one after the other on st when no side stream
+// can be made.
+template <typename StateChain>
+static hipError_t run_two_chains(const BwdParams& p, int dk, int dv, hipStream_t st, StateChain state_chain) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    SideStream* sd = (dev >= 0 && dev < kMaxSideDevices) ? &side_stream(dev) : nullptr;
+    std::unique_lock<std::mutex> lk;
+    if (sd) {
+        lk = std::unique_lock<std::mutex>(sd->m);
+        if (side_init(*sd) != hipSuccess) {
+            // no second stream (e.g. first use inside a graph capture that forbids
+            // creating one): the reverse chain runs after the state chain instead
+            (void)hipGetLastError();
+            sd = nullptr;
+        }
+    }
+    if (sd) {
+        e = hipEventRecord(sd->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+        if (e == hipSuccess) e = launch_bwd_dchain(p, dk, dv, p.records, sd->s);
+        if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
+        if (e == hipSuccess) e = state_chain();
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, sd->join, 0);
+    } else {
+        e = launch_bwd_dchain(p, dk, dv, p.records, st);
+        if (e == hipSuccess) e = state_chain();
+    }
+    return e;
+}
+
 // the two-pass path keeps S' and the state gradients as f16 fragments, the
 // generic path as fp32 rows
 static bool bwd_two_pass(int dk, int dv, int T, int cb, uint32_t flags) {
@@ -947,31 +981,7 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
         f.state_frags = p.state_frags;
         e = launch_fwd_wy(f, dk, dv, p.records, st, true, kWyPass);
         if (e != hipSuccess) return e;
-        int dev = 0;
-        e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        SideStream* sd = (dev >= 0 && dev < kMaxSideDevices) ? &side_stream(dev) : nullptr;
-        std::unique_lock<std::mutex> lk;
-        if (sd) {
-            lk = std::unique_lock<std::mutex>(sd->m);
-            if (side_init(*sd) != hipSuccess) {
-                // no second stream (e.g. first use inside a graph capture that forbids
-                // creating one): the reverse chain runs after the state chain instead
-                (void)hipGetLastError();
-                sd = nullptr;
-            }
-        }
-        if (sd) {
-            e = hipEventRecord(sd->fork, st);
-            if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
-            if (e == hipSuccess) e = launch_bwd_dchain(p, dk, dv, p.records, sd->s);
-            if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
-            if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);
-            if (e == hipSuccess) e = hipStreamWaitEvent(st, sd->join, 0);
-        } else {
-            e = launch_bwd_dchain(p, dk, dv, p.records, st);
-            if (e == hipSuccess) e = launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass);
-        }
+        e = run_two_chains(p, dk, dv, st, [&] { return launch_fwd_wy(f, dk, dv, p.records, st, true, kChainPass); });
         if (e != hipSuccess) return e;
         return launch_bwd_wgrad(p, dk, dv, p.records, st);
     }
@@ -989,6 +999,45 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
     }
     if (f32) return bwd::launch_t<64, 64, 32, true>(p, st, ds);
     return cb == 64 ? bwd::launch_t<64, 64, 64, false>(p, st, ds) : bwd::launch_t<64, 64, 32, false>(p, st, ds);
+}
+
+// Packed sequences: the same three steps over the packed records, S' and D
+// fragments (numbered head * chunk count + chunk), after the prep step.
+static size_t packed_rec_bytes(int dk, int dv) { return fwd_wy_workspace_bytes(1, 64, dk, dv, true); }
+
+size_t bwd_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv) {
+    if (H < 1 || nseq < 1 || T < 0 || dk != dv || !(dk == 64 || dk == 128)) return 0;
+    const size_t per_chunk = packed_rec_bytes(dk, dv) + 2 * (size_t)dk * dv * 2;
+    return (size_t)H * packed_max_chunks(T, nseq) * per_chunk + packed_prep_bytes(T, nseq);
+}
+
+hipError_t launch_bwd_varlen(const BwdParams& p0, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st) {
+    const size_t need = bwd_varlen_workspace_bytes(p0.BH, p0.T, p0.nseq, dk, dv);
+    if (need == 0 || ws_bytes < need || !p0.cu_seqlens || !fwd_wy_supported(dk, dv, 64, p0.flags))
+        return hipErrorInvalidValue;
+    BwdParams p = p0;
+    const size_t n = (size_t)p.BH * packed_max_chunks(p.T, p.nseq);
+    const size_t recb = n * packed_rec_bytes(dk, dv), fragb = n * (size_t)dk * dv * 2;
+    unsigned char* base = reinterpret_cast<unsigned char*>(ws);
+    p.records = base;
+    p.state_frags = base + recb;
+    p.dstate_frags = base + recb + fragb;
+    int *off = nullptr, *tab = nullptr, *ord = nullptr;
+    hipError_t e = launch_packed_prep(p.cu_seqlens, p.nseq, p.T, base + recb + 2 * fragb, &off, &tab, &ord, st);
+    if (e != hipSuccess) return e;
+    p.chunk_off = off;
+    p.chunk_tab = tab;
+    p.seq_order = ord;
+    FwdParams f;
+    f.q = p.q; f.k = p.k; f.v = p.v; f.la = p.la; f.b = p.b; f.w = p.w; f.S0 = p.S0;
+    f.o = nullptr; f.Sf = nullptr; f.states = nullptr; f.state_frags = p.state_frags;
+    f.cu_seqlens = p.cu_seqlens; f.chunk_off = off; f.chunk_tab = tab; f.seq_order = ord; f.nseq = p.nseq;
+    f.BH = p.BH; f.T = p.T; f.flags = p.flags & ~(uint32_t)GDR_OUT_BF16;
+    e = launch_fwd_wy_packed(f, dk, dv, p.records, st, true, kWyPass);
+    if (e != hipSuccess) return e;
+    e = run_two_chains(p, dk, dv, st, [&] { return launch_fwd_wy_packed(f, dk, dv, p.records, st, true, kChainPass); });
+    if (e != hipSuccess) return e;
+    return launch_bwd_wgrad(p, dk, dv, p.records, st);
 }
 
 }  // namespace gdr

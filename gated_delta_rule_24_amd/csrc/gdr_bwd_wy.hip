@@ -35,7 +35,7 @@ struct FFrags {
     uint32_t dob[NK2][8];       // raw bf16 dO values (K = tokens)
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool VL>
 __global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsigned char* ws) {
     using R = Rec<DK, DV>;
     constexpr size_t RB = R::bwd_bytes;
@@ -43,10 +43,27 @@ __global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsig
     __shared__ __align__(16) floatx4 sF[2][NKT][64];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = lid / NST, nt = lid % NST;
-    const int NC = p.T / C;
-    const unsigned char* rec0 = ws + (size_t)bh * NC * RB;
+    // chain bh (packed sequences: sequence bh / H of head bh % H, the longest
+    // first) and its 16-column strip nt
+    int bh, nt, NC, seq_len;
+    size_t tok_base, chunk0;
+    if constexpr (VL) {
+        bh = packed_chain(p.seq_order, p.BH, NST, (int)blockIdx.x, (int)gridDim.x, nt);
+        const PackedSpan sp = packed_span(p.cu_seqlens, p.chunk_off, p.nseq, p.BH, p.T, bh);
+        NC = sp.NC;
+        seq_len = sp.len;
+        tok_base = sp.tok0;
+        chunk0 = sp.chunk0;
+    } else {
+        const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        bh = lid / NST;
+        nt = lid % NST;
+        NC = p.T / C;
+        seq_len = p.T;
+        tok_base = (size_t)bh * p.T;
+        chunk0 = (size_t)bh * NC;
+    }
+    const unsigned char* rec0 = ws + chunk0 * RB;
     const int n_l = lane & 15, g4 = 4 * (lane >> 4), col = 16 * nt + n_l;
     auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
         return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
@@ -66,13 +83,16 @@ __global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsig
             for (int mt = 0; mt < NKT; ++mt)
 #pragma unroll
                 for (int kk = 0; kk < NK2; ++kk) f.qt[mt][kk] = frag(rec, R::QT + (size_t)(mt * NK2 + kk) * 1024);
-            const size_t tok0 = (size_t)bh * p.T + (size_t)cc * C;
+            const size_t tok0 = tok_base + (size_t)cc * C;
 #pragma unroll
             for (int kk = 0; kk < NK2; ++kk)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
+                    // (packed sequences: rows past the sequence's end read as zero)
                     const int t = 32 * kk + (j < 4 ? g4 + j : 16 + g4 + j - 4);
-                    f.dob[kk][j] = dO[(tok0 + t) * DV + col];
+                    const bool ok = !VL || cc * C + t < seq_len;
+                    f.dob[kk][j] = dO[(tok0 + (ok ? t : 0)) * DV + col];
+                    if (!ok) f.dob[kk][j] = 0;
                 }
         };
         auto compute = [&](F& f, int buf) __attribute__((always_inline)) {
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsig
         for (int kk = 0; kk < NKK; ++kk) df[kk] = cat8(to_h4(D[2 * kk]), to_h4(D[2 * kk + 1]));
         {
             using SFB = StateFrag<DK, DV>;
-            unsigned char* dst = reinterpret_cast<unsigned char*>(p.dstate_frags) + ((size_t)bh * NC + c) * SFB::bytes;
+            unsigned char* dst = reinterpret_cast<unsigned char*>(p.dstate_frags) + (chunk0 + c) * SFB::bytes;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
                 *reinterpret_cast<half8*>(dst + SFB::block(nt, kk) + (size_t)lane * 16) = poisoned ? nan8 : df[kk];
@@ -204,8 +224,14 @@ __global__ __launch_bounds__(128, 1) void dchain_kernel(BwdParams p, const unsig
 
 template <int DK, int DV>
 static hipError_t launch_dchain(const BwdParams& p, const void* ws, hipStream_t st) {
-    hipLaunchKernelGGL((dchain_kernel<DK, DV>), dim3((unsigned)(p.BH * (DV / 16))), dim3(128), 0, st, p,
-                       reinterpret_cast<const unsigned char*>(ws));
+    const unsigned char* rec = reinterpret_cast<const unsigned char*>(ws);
+    if (p.cu_seqlens) {
+        hipLaunchKernelGGL((dchain_kernel<DK, DV, true>), dim3((unsigned)(p.nseq * p.BH * (DV / 16))), dim3(128), 0,
+                           st, p, rec);
+    } else {
+        hipLaunchKernelGGL((dchain_kernel<DK, DV, false>), dim3((unsigned)(p.BH * (DV / 16))), dim3(128), 0, st, p,
+                           rec);
+    }
     return hipGetLastError();
 }
 
@@ -332,7 +358,7 @@ __device__ __forceinline__ void chunk_decay(const floatx4 (&la)[4], floatx4 (&gm
     for (int tt = 0; tt < 4; ++tt) gm[tt] -= carry;
 }
 
-template <int D, bool AS, bool BS, bool WS>
+template <int D, bool AS, bool BS, bool WS, bool VL>
 __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsigned char* ws) {
     using R = Rec<D, D>;
     using SFB = StateFrag<D, D>;
@@ -355,10 +381,27 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = 4 * (lane >> 4);
-    const int NC = p.T / C;
-    const int bh = (int)blockIdx.x / NC, c = (int)blockIdx.x % NC;
-    const size_t chunk = (size_t)bh * NC + c;
-    const size_t tok0 = (size_t)bh * p.T + (size_t)c * C;
+    // this workgroup's chunk: its record/fragment index, first token and length
+    // (packed sequences: chunk r of head h from the chunk table; rows past the
+    // sequence's end load as zeros and store nothing)
+    size_t chunk, tok0;
+    int len;
+    if constexpr (VL) {
+        const int CN = p.chunk_off[p.nseq];
+        const int idx = (int)blockIdx.x;
+        if (idx >= p.BH * CN) return;                // grid sized for the largest chunk count
+        const int h = idx / CN, r = idx - h * CN;
+        const int2 e = reinterpret_cast<const int2*>(p.chunk_tab)[r];
+        chunk = (size_t)h * CN + r;
+        tok0 = (size_t)h * p.T + (size_t)e.x;
+        len = e.y;
+    } else {
+        const int NC = p.T / C;
+        const int bh = (int)blockIdx.x / NC, c = (int)blockIdx.x % NC;
+        chunk = (size_t)bh * NC + c;
+        tok0 = (size_t)bh * p.T + (size_t)c * C;
+        len = C;
+    }
     const unsigned char* rec = ws + chunk * RB;
     const unsigned char* sfr = reinterpret_cast<const unsigned char*>(p.state_frags) + chunk * SFB::bytes;
     const unsigned char* dfr = reinterpret_cast<const unsigned char*>(p.dstate_frags) + chunk * SFB::bytes;
@@ -411,11 +454,14 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     uint2 vr[NB], wr[NB], dor[NB];
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-        const int t = 16 * rt + r16, ix = t * D + 16 * vt + g4;
+        const int t0 = 16 * rt + r16;
+        const bool ok = !VL || t0 < len;
+        const int t = ok ? t0 : 0, ix = t * D + 16 * vt + g4;
         vr[rt] = *reinterpret_cast<const uint2*>(vg + ix);
         if constexpr (WS) wr[rt].x = wg[t];
         else wr[rt] = *reinterpret_cast<const uint2*>(wg + ix);
         dor[rt] = *reinterpret_cast<const uint2*>(og + ix);
+        if (!ok) vr[rt] = wr[rt] = dor[rt] = make_uint2(0u, 0u);
     }
     // Ũ (this wave's value tile) and the state fragments of the channel loop
     half8 fur[NK2], fsa[NKK], fda[NKK];
@@ -491,11 +537,12 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         *reinterpret_cast<half4*>(sR + (16 * rt + r16) * LDX + 16 * vt + g4) = to_h4(t1);
         const floatx4 x = mfma16(to_h4(dR[rt] - f4(hi)), id, t1);
         const int ix = (16 * rt + r16) * D + 16 * vt + g4;
+        const bool ok = !VL || 16 * rt + r16 < len;
         const floatx4 v4 = cvt_raw4<false>(Raw4<false>{vr[rt]});
         const floatx4 w4 = WS ? splat4(bf16_to_f32((uint16_t)wr[rt].x)) : cvt_raw4<false>(Raw4<false>{wr[rt]});
-        *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
+        if (ok) *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
         if constexpr (WS) dwp[rt] = hsum4(x * v4);
-        else *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
+        else if (ok) *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
     }
     if constexpr (WS) {
 #pragma unroll
@@ -512,12 +559,18 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     uint2 qr[NB], kr[NB], brw[NB];
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-        const int t = 16 * tt + r16, ix = t * D + 16 * ct + g4;
+        const int t0 = 16 * tt + r16;
+        const bool ok = !VL || t0 < len;
+        const int t = ok ? t0 : 0, ix = t * D + 16 * ct + g4;
         lar[tt] = AS ? splat4(lag[t]) : *reinterpret_cast<const floatx4*>(lag + ix);
         qr[tt] = *reinterpret_cast<const uint2*>(qg + ix);
         kr[tt] = *reinterpret_cast<const uint2*>(kg + ix);
         if constexpr (BS) brw[tt].x = bg[t];
         else brw[tt] = *reinterpret_cast<const uint2*>(bg + ix);
+        if (!ok) {
+            lar[tt] = zero4();
+            qr[tt] = kr[tt] = brw[tt] = make_uint2(0u, 0u);
+        }
     }
     lds_barrier();
     // S' and D (this wave's value tile, all channels) into LDS with channels as
@@ -684,21 +737,25 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
         const int ix = (16 * tt + r16) * D + 16 * ct + g4;
+        const bool ok = !VL || 16 * tt + r16 < len;
         const floatx4 eg = expv4(gm[tt]), ek = expv4(-gm[tt]);
         const floatx4 q4 = cvt_raw4<false>(Raw4<false>{qr[tt]}), k4 = cvt_raw4<false>(Raw4<false>{kr[tt]});
         const floatx4 b4 = BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]});
         const floatx4 dQs = A1[tt], dE = -A2[tt], dKh = A3[tt];
-        *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
-        *reinterpret_cast<floatx4*>(dkg + ix) = dE * b4 * eg + dKh * ek + poison;
+        if (ok) {
+            *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
+            *reinterpret_cast<floatx4*>(dkg + ix) = dE * b4 * eg + dKh * ek + poison;
+        }
         const floatx4 dbv = dE * k4 * eg;
         if constexpr (BS) dbs[tt] = hsum4(dbv);
-        else *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
+        else if (ok) *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
         const floatx4 dg = dE * (b4 * k4 * eg) + dQs * (q4 * eg) - dKh * (k4 * ek);
         if constexpr (AS) {
             dgs[tt] = hsum4(dg);
         } else {
             // d log alpha = Phi - (exclusive prefix of dg over the tokens)
-            *reinterpret_cast<floatx4*>(dlag + ix) = phi - (carry + (scan16(dg) - dg)) + poison;
+            const floatx4 dla = phi - (carry + (scan16(dg) - dg)) + poison;
+            if (ok) *reinterpret_cast<floatx4*>(dlag + ix) = dla;
             carry += rowsum16(dg);
         }
     }
@@ -733,8 +790,15 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
                 for (int w = 0; w < NW; ++w) a += sRed[(which * NW + w) * C + t];
                 return a;
             };
-            if constexpr (WS) dwg[t] = wsum(0) + poison;
-            if constexpr (BS) dbg[t] = wsum(1) + poison;
+            const bool ok = !VL || t < len;
+            if constexpr (WS) {
+                const float v = wsum(0) + poison;
+                if (ok) dwg[t] = v;
+            }
+            if constexpr (BS) {
+                const float v = wsum(1) + poison;
+                if (ok) dbg[t] = v;
+            }
             if constexpr (AS) {
                 const float dg = wsum(2);
                 float incl = dg;
@@ -746,16 +810,15 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
                 float ptot = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) ptot += sPhi[w];
-                dlag[t] = ptot - (incl - dg) + poison;
+                if (ok) dlag[t] = ptot - (incl - dg) + poison;
             }
         }
     }
 }
 
-template <int D, bool AS, bool BS, bool WS>
-static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t st) {
-    const int NC = p.T / C;
-    auto k = wgrad_kernel<D, AS, BS, WS>;
+template <int D, bool AS, bool BS, bool WS, bool VL>
+static hipError_t launch_wgrad_v(const BwdParams& p, const void* ws, hipStream_t st) {
+    auto k = wgrad_kernel<D, AS, BS, WS, VL>;
     static bool attr_done = false;
     if (!attr_done) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -764,9 +827,17 @@ static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipLaunchKernelGGL(k, dim3((unsigned)(p.BH * NC)), dim3(D * 4), WgradLayout<D>::bytes, st, p,
+    // packed sequences: the chunk count is on the device; the grid covers the
+    // largest possible count and the workgroups past the real one return at once
+    const size_t items = VL ? (size_t)p.BH * packed_max_chunks(p.T, p.nseq) : (size_t)p.BH * (p.T / C);
+    hipLaunchKernelGGL(k, dim3((unsigned)items), dim3(D * 4), WgradLayout<D>::bytes, st, p,
                        reinterpret_cast<const unsigned char*>(ws));
     return hipGetLastError();
+}
+
+template <int D, bool AS, bool BS, bool WS>
+static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t st) {
+    return p.cu_seqlens ? launch_wgrad_v<D, AS, BS, WS, true>(p, ws, st) : launch_wgrad_v<D, AS, BS, WS, false>(p, ws, st);
 }
 
 template <int D>

@@ -628,22 +628,10 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // chain bh: a (batch, head) sequence, or for packed sequences sequence
     // bh / H of head bh % H (its state is S0[bh], as [nseq, H] is laid out)
+    // (packed sequences: chains of very different lengths, the longest first)
     int bh, ng;                                          // strips NS*ng .. NS*ng+NS-1
     if constexpr (VL) {
-        // packed sequences: chains of very different lengths.  The longest go
-        // first (seq_order), dealt round-robin over the XCDs (workgroup b runs
-        // on XCD b % 8) with the strips of one chain kept on one XCD.
-        const int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
-        int rank;
-        if (nblk % (8 * NGRP) == 0) {
-            const int pos = bid / 8;
-            rank = (pos / NGRP) * 8 + bid % 8;
-            ng = pos % NGRP;
-        } else {
-            rank = bid / NGRP;
-            ng = bid % NGRP;
-        }
-        bh = p.seq_order[rank / p.BH] * p.BH + rank % p.BH;
+        bh = packed_chain(p.seq_order, p.BH, NGRP, (int)blockIdx.x, (int)gridDim.x, ng);
     } else {
         const int lid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
         bh = lid / NGRP;
@@ -651,20 +639,20 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
     }
     int NC, seq_len;
     size_t tok_base;                                     // the chain's first token
-    const unsigned char* rec0;
+    size_t chunk0;                                       // its first chunk (records, fragments)
     if constexpr (VL) {
-        const int s = bh / p.BH, h = bh % p.BH;
-        const int c0 = p.chunk_off[s];
-        NC = p.chunk_off[s + 1] - c0;
-        seq_len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
-        tok_base = (size_t)h * p.T + (size_t)p.cu_seqlens[s];
-        rec0 = ws + ((size_t)h * p.chunk_off[p.nseq] + c0) * RB;
+        const PackedSpan sp = packed_span(p.cu_seqlens, p.chunk_off, p.nseq, p.BH, p.T, bh);
+        NC = sp.NC;
+        seq_len = sp.len;
+        tok_base = sp.tok0;
+        chunk0 = sp.chunk0;
     } else {
         NC = p.T / C;
         seq_len = p.T;
         tok_base = (size_t)bh * p.T;
-        rec0 = ws + (size_t)bh * NC * RB;
+        chunk0 = (size_t)bh * NC;
     }
+    const unsigned char* rec0 = ws + chunk0 * RB;
     const int n_l = lane & 15, g4 = 4 * (lane >> 4);
     auto frag = [&](const unsigned char* rec, size_t off) __attribute__((always_inline)) {
         return *reinterpret_cast<const half8*>(rec + off + (size_t)lane * 16);
@@ -875,7 +863,7 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
         if (p.state_frags) {
             // the backward's copy of S' (after an out-of-range chunk: NaN)
             using SFB = StateFrag<DK, DV>;
-            unsigned char* dst = reinterpret_cast<unsigned char*>(p.state_frags) + ((size_t)bh * NC + c) * SFB::bytes;
+            unsigned char* dst = reinterpret_cast<unsigned char*>(p.state_frags) + (chunk0 + c) * SFB::bytes;
             half8 nan8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) nan8[e] = (_Float16)__builtin_nanf("");
@@ -1105,13 +1093,53 @@ static size_t varlen_rec_bytes(int dk, int dv) {
 
 static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
+size_t packed_max_chunks(long long T, int nseq) {
+    // every sequence has at most len / C + 1 chunks
+    return (size_t)(T / wy::C) + (size_t)nseq;
+}
+
+size_t packed_prep_bytes(long long T, int nseq) {
+    return round256(((size_t)nseq + 1) * sizeof(int)) + round256(packed_max_chunks(T, nseq) * 2 * sizeof(int)) +
+           round256((size_t)nseq * sizeof(int));
+}
+
+hipError_t launch_packed_prep(const int* cu_seqlens, int nseq, long long T, void* mem, int** chunk_off,
+                              int** chunk_tab, int** seq_order, hipStream_t st) {
+    unsigned char* m = reinterpret_cast<unsigned char*>(mem);
+    const size_t max_chunks = packed_max_chunks(T, nseq);
+    *chunk_off = reinterpret_cast<int*>(m);
+    m += round256(((size_t)nseq + 1) * sizeof(int));
+    *chunk_tab = reinterpret_cast<int*>(m);
+    m += round256(max_chunks * 2 * sizeof(int));
+    *seq_order = reinterpret_cast<int*>(m);
+    hipLaunchKernelGGL(wy::varlen_chunk_offsets, dim3(1), dim3(1024), 0, st, cu_seqlens, nseq, *chunk_off,
+                       *seq_order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wy::varlen_chunk_table, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, st,
+                       cu_seqlens, *chunk_off, nseq, (int)max_chunks, *chunk_tab);
+    return hipGetLastError();
+}
+
 size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv) {
     const size_t rb = varlen_rec_bytes(dk, dv);
     if (rb == 0 || H < 1 || nseq < 1 || T < 0) return 0;
-    // every sequence has at most len / C + 1 chunks
-    const size_t max_chunks = (size_t)(T / wy::C) + (size_t)nseq;
-    return (size_t)H * max_chunks * rb + round256(((size_t)nseq + 1) * sizeof(int)) +
-           round256(max_chunks * 2 * sizeof(int)) + round256((size_t)nseq * sizeof(int));
+    return (size_t)H * packed_max_chunks(T, nseq) * rb + packed_prep_bytes(T, nseq);
+}
+
+hipError_t launch_fwd_wy_packed(const FwdParams& p, int dk, int dv, void* records, hipStream_t st,
+                                bool bwd_layouts, int passes) {
+    if (!p.cu_seqlens || !p.chunk_off || !p.chunk_tab || !p.seq_order) return hipErrorInvalidValue;
+    if (bwd_layouts) {
+        if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, true, true>(p, records, st, passes);
+        if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, true, true>(p, records, st, passes);
+        return hipErrorInvalidValue;
+    }
+    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false, true>(p, records, st, passes);
+    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false, true>(p, records, st, passes);
+    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false, true>(p, records, st, passes);
+    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false, true>(p, records, st, passes);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_wy_varlen(const FwdParams& p0, int dk, int dv, void* ws, size_t ws_bytes,
@@ -1120,27 +1148,10 @@ hipError_t launch_fwd_wy_varlen(const FwdParams& p0, int dk, int dv, void* ws, s
     if (need == 0 || ws_bytes < need || !p0.cu_seqlens) return hipErrorInvalidValue;
     FwdParams p = p0;
     const size_t rb = varlen_rec_bytes(dk, dv);
-    const size_t max_chunks = (size_t)(p.T / wy::C) + (size_t)p.nseq;
-    unsigned char* tail = reinterpret_cast<unsigned char*>(ws) + (size_t)p.BH * max_chunks * rb;
-    p.chunk_off = reinterpret_cast<int*>(tail);
-    tail += round256(((size_t)p.nseq + 1) * sizeof(int));
-    p.chunk_tab = reinterpret_cast<int*>(tail);
-    tail += round256(max_chunks * 2 * sizeof(int));
-    p.seq_order = reinterpret_cast<int*>(tail);
-    hipLaunchKernelGGL(wy::varlen_chunk_offsets, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.nseq, p.chunk_off,
-                       p.seq_order);
-    hipError_t e = hipGetLastError();
+    unsigned char* prep = reinterpret_cast<unsigned char*>(ws) + (size_t)p.BH * packed_max_chunks(p.T, p.nseq) * rb;
+    hipError_t e = launch_packed_prep(p.cu_seqlens, p.nseq, p.T, prep, &p.chunk_off, &p.chunk_tab, &p.seq_order, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wy::varlen_chunk_table, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, st,
-                       p.cu_seqlens, p.chunk_off, p.nseq, (int)max_chunks, p.chunk_tab);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int passes = kWyPass | kChainPass;
-    if (dk == 128 && dv == 128) return wy::launch_modes<128, 128, false, true>(p, ws, st, passes);
-    if (dk == 64 && dv == 64) return wy::launch_modes<64, 64, false, true>(p, ws, st, passes);
-    if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false, true>(p, ws, st, passes);
-    if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false, true>(p, ws, st, passes);
-    return hipErrorInvalidValue;
+    return launch_fwd_wy_packed(p, dk, dv, ws, st, false, kWyPass | kChainPass);
 }
 
 }  // namespace gdr

@@ -70,9 +70,18 @@ size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts = 
 constexpr int kWyPass = 1, kChainPass = 2;
 hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st,
                          bool bwd_layouts = false, int passes = kWyPass | kChainPass);
-// Packed variable-length sequences: workspace bytes (records of at most
-// T/64 + nseq chunks per head, then the chunk offsets and the chunk table), and
-// the two passes.
+// Packed variable-length sequences.  Each head holds at most T/64 + nseq
+// chunks; records and fragments are numbered head * (chunk count) + chunk.
+// The prep step fills, in prep_bytes of device memory: the chunk offsets of
+// the sequences, the chunk table and the longest-first sequence order.
+size_t packed_max_chunks(long long T, int nseq);
+size_t packed_prep_bytes(long long T, int nseq);
+hipError_t launch_packed_prep(const int* cu_seqlens, int nseq, long long T, void* mem, int** chunk_off,
+                              int** chunk_tab, int** seq_order, hipStream_t st);
+// The two passes over packed sequences (p's prep pointers set).
+hipError_t launch_fwd_wy_packed(const FwdParams& p, int dk, int dv, void* records, hipStream_t st,
+                                bool bwd_layouts, int passes);
+// The whole packed forward: workspace = records, then the prep arrays.
 size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
 hipError_t launch_fwd_wy_varlen(const FwdParams& p, int dk, int dv, void* ws, size_t ws_bytes,
                                 hipStream_t st);
@@ -99,9 +108,15 @@ struct BwdParams {
     void* records;         // workspace: per-chunk WY operands of the two-pass forward (or null)
     void* state_frags;     // workspace, two-pass path: S' per chunk, f16 fragments
     void* dstate_frags;    // workspace, two-pass path: chunk-end state gradients, f16 fragments
-    int BH;
+    int BH;                // packed sequences: BH = H heads, T = total tokens per head
     int T;
     uint32_t flags;
+    // packed variable-length sequences (as FwdParams), or null
+    const int* cu_seqlens;
+    const int* chunk_off;
+    const int* chunk_tab;
+    const int* seq_order;
+    int nseq;
 };
 
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
@@ -113,5 +128,9 @@ hipError_t launch_bwd_wgrad(const BwdParams& p, int dk, int dv, const void* reco
 size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
 bool bwd_supported(int dk, int dv, int chunk, uint32_t flags);
 hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t st);
+// Packed sequences (bf16, d_k == d_v in {64, 128}): workspace = records, S'
+// fragments, D fragments (each for packed_max_chunks per head), prep arrays.
+size_t bwd_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
+hipError_t launch_bwd_varlen(const BwdParams& p, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace gdr

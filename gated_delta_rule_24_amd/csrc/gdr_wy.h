@@ -129,5 +129,39 @@ __device__ __forceinline__ half4 ld_col4(const _Float16* p, int ld) {
     return h;
 }
 
+// Packed sequences: the chain that workgroup bid of nblk serves, as sequence *
+// H + head, and its strip ng of NG.  The longest sequences go first (order),
+// dealt round-robin over the XCDs (workgroup b runs on XCD b % 8), with the NG
+// strips of one chain on one XCD so that they share its L2.
+__device__ __forceinline__ int packed_chain(const int* order, int H, int NG, int bid, int nblk, int& ng) {
+    int rank;
+    if (nblk % (8 * NG) == 0) {
+        const int pos = bid / 8;
+        rank = (pos / NG) * 8 + bid % 8;
+        ng = pos % NG;
+    } else {
+        rank = bid / NG;
+        ng = bid % NG;
+    }
+    return order[rank / H] * H + rank % H;
+}
+
+// Packed sequences: the chunks of chain bh (sequence bh / H of head bh % H):
+// their count, the sequence's length, its first token in the [H, T] streams
+// and its first chunk in the per-head chunk numbering (records, fragments).
+struct PackedSpan {
+    int NC, len;
+    size_t tok0, chunk0;
+};
+__device__ __forceinline__ PackedSpan packed_span(const int* cu, const int* off, int nseq, int H, int T, int bh) {
+    const int s = bh / H, h = bh % H;
+    PackedSpan r;
+    r.NC = off[s + 1] - off[s];
+    r.len = cu[s + 1] - cu[s];
+    r.tok0 = (size_t)h * T + (size_t)cu[s];
+    r.chunk0 = (size_t)h * off[nseq] + (size_t)off[s];
+    return r;
+}
+
 }  // namespace wy
 }  // namespace gdr

@@ -217,6 +217,39 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v,
                          uint32_t flags, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * The backward of gdr_chunk_fwd_varlen (packed variable-length sequences,
+ * "Gated DeltaNet study notes" §4-3), for the same loss: every sequence's
+ * gradients depend only on its own tokens, initial state and dS_final.
+ *
+ *   inputs as gdr_chunk_fwd_varlen ([H, T, ...] token streams, cu_seqlens in
+ *   DEVICE memory with the same guarantees), plus
+ *   dO         : act  [H, T, d_v]
+ *   dS_final   : fp32 [nseq, H, d_k, d_v]; NULL means zero
+ *   outputs (fp32, written, never accumulated into):
+ *   dq, dk     : [H, T, d_k]       dv : [H, T, d_v]
+ *   dlog_alpha, db, dw : [H, T, d_k] / [H, T, d_k] / [H, T, d_v], or [H, T]
+ *                in the scalar modes (as gdr_chunk_bwd)
+ *   dS0        : [nseq, H, d_k, d_v]; may be NULL.  A sequence of length 0
+ *                gets dS0 = dS_final (zero when dS_final is NULL).
+ *   workspace  : required, at least gdr_chunk_bwd_varlen_workspace_bytes()
+ *                bytes, owned by the caller; contents on entry are ignored.
+ * Uses the library's second stream as gdr_chunk_bwd does.
+ * Supported: bf16 activations, d_k = d_v = 128 or 64 (chunks of 64).
+ * Returns GDR_ERR_UNSUPPORTED otherwise.
+ */
+size_t gdr_chunk_bwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v,
+                                            uint32_t flags);
+
+gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* b, const void* w,
+                                const float* S0, const void* dO, const float* dS_final,
+                                float* dq, float* dk, float* dv, float* dlog_alpha,
+                                float* db, float* dw, float* dS0,
+                                const int* cu_seqlens, int nseq, int H, int T,
+                                int d_k, int d_v, uint32_t flags, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -167,3 +167,42 @@ def test_fwd_varlen_workspace_query():
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0   # fp32
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 32, 32, 0) == 0
+
+
+def _bwd_varlen(lib, **kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, dO=A, dSf=None, dq=A, dk_=A, dv_=A,
+                dla=A, db=A, dw=A, dS0=None, cu=A, nseq=2, H=1, T=100, dk=128, dv=128, flags=0,
+                ws=A, nbytes=1 << 30)
+    args.update(kw)
+    a = args
+    return lib.gdr_chunk_bwd_varlen(a["q"], a["k"], a["v"], a["la"], a["b"], a["w"], a["S0"],
+                                    a["dO"], a["dSf"], a["dq"], a["dk_"], a["dv_"], a["dla"],
+                                    a["db"], a["dw"], a["dS0"], a["cu"], a["nseq"], a["H"],
+                                    a["T"], a["dk"], a["dv"], a["flags"], a["ws"], a["nbytes"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), 1), (dict(dq=None), 1), (dict(cu=None), 1), (dict(nseq=0), 1),
+    (dict(T=-1), 1), (dict(flags=0x2), 1), (dict(dla=MIS), 1), (dict(dS0=MIS), 1),
+    (dict(ws=None), 3), (dict(nbytes=4096), 3), (dict(H=1 << 20, T=1 << 20), 1),
+    (dict(dk=128, dv=64), 2), (dict(dk=32, dv=32), 2), (dict(flags=0x1), 2),
+])
+def test_bwd_varlen_argument_validation(kw, status):
+    assert _bwd_varlen(_lib(), **kw) == status
+
+
+def test_bwd_varlen_workspace_query():
+    lib = _lib()
+    # per chunk slot (H * (T//64 + nseq) of them): the forward record with the
+    # backward's layouts, S' and the state gradient as f16 (2 x d_k x d_v x 2
+    # bytes); then the prep arrays as for the packed forward
+    rec = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0) - 2 * 128 * 128 * 2
+    slot = rec + 2 * 128 * 128 * 2
+    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(3, 2, 200, 128, 128, 0) == 2 * 6 * slot + 768
+    rec64 = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0) - 2 * 64 * 64 * 2
+    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 4, 128, 64, 64, 0x1c) == \
+        4 * 3 * (rec64 + 2 * 64 * 64 * 2) + 768
+    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 64, 0) == 0
+    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0
+    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
