@@ -44,7 +44,11 @@
  *   MFMA with f16 operands and fp32 accumulation; the state, log-decay and
  *   the cumulative decay stay fp32 (the log-decay path runs in fp32:
  *   "Gated DeltaNet-2 Review" §3-2 item 2).  With fp32 activations every
- *   contraction runs on fp32 MFMA.
+ *   contraction runs on fp32 MFMA.  Erase gates up to 2 (the expanded range,
+ *   "Gated DeltaNet-2 Review" §5) keep the bf16 accuracy for ordinary keys;
+ *   one key repeated through a chunk with an erase gate near 2 makes the
+ *   in-chunk solve cancel by about two orders of magnitude, and such inputs
+ *   need fp32 activations.
  */
 #ifndef GDR_H
 #define GDR_H

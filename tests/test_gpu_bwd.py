@@ -208,3 +208,22 @@ def test_gdn_backward_workload_shape_sampled_heads():
     _check(inp, got, _ref(inp, heads=heads), 2e-2, heads=heads)
     for n in GRADS:
         assert np.isfinite(got[n]).all(), n
+
+
+
+@pytest.mark.parametrize("act,tol,repeat_key", [("bf16", 2e-2, False), ("f32", 1e-3, True)],
+                         ids=["bf16_random_keys", "f32_repeated_key"])
+def test_backward_full_erase_gate(act, tol, repeat_key):
+    """b = 2 everywhere (the end of the expanded erase range): bf16 with
+    model-like keys, and one key repeated through each head with fp32
+    activations. The repeated key is the worst case for the in-chunk solve:
+    its solution cancels by about two orders of magnitude, so it needs fp32
+    operands. Being a stress case outside the pages' workloads, it is held to
+    1e-3 (measured 1e-5 to 2.3e-4)."""
+    inp = _case("full_erase", B=1, H=2, T=192, dk=128, dv=128, act=act)
+    a = inp.arrays
+    a["b"] = np.full_like(a["b"], 2.0)
+    if repeat_key:
+        a["k"] = np.ascontiguousarray(np.broadcast_to(a["k"][:, :, :1], a["k"].shape))
+    dSf = _dsf(inp)
+    _check(inp, _run(inp, dSf), _ref(inp, dSf), tol)

@@ -250,3 +250,40 @@ def test_gdn_full_workload_sampled_heads():
     inp = _case("gdn")
     o, sf = _run(inp)
     _check(inp, o, sf, 2e-2, heads=[0, 13, 40, 63])
+
+
+
+def _full_erase(inp, repeat_key=False):
+    """b = 2 on every channel of every token (the end of the expanded erase
+    range, where the erase factor reflects along k); optionally the same key
+    at every token of a head, the worst case for the in-chunk solve."""
+    a = inp.arrays
+    a["b"] = np.full_like(a["b"], 2.0)
+    if repeat_key:
+        a["k"] = np.ascontiguousarray(np.broadcast_to(a["k"][:, :, :1], a["k"].shape))
+    return inp
+
+
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_full_erase_gate(path):
+    """b = 2 everywhere with model-like (random unit) keys: within the bf16
+    tolerance on both forward paths."""
+    inp = _full_erase(_case("full_erase", B=1, H=2, T=256, dk=128, dv=128))
+    o, sf = _run(inp, path=path)
+    _check(inp, o, sf, 2e-2)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_full_erase_repeated_key_fp32(chunk):
+    """One key repeated through every token at b = 2: inside a chunk the
+    solution of (I + A) U = X - E S' alternates in sign with entries about
+    2 sqrt(C) times |x|, which the state update then sums back to O(|x|).
+    That cancellation amplifies rounding by about two orders of magnitude: f16
+    operands lose about 10% (bf16 activations: 0.10-0.15 at chunks 16-64).
+    Such inputs need fp32 activations. This stress case is not one of the
+    pages' workloads, for which the fp32 tolerance is 1e-4; it is held to
+    1e-3 here (measured about 1e-4)."""
+    inp = _full_erase(_case("full_erase_rk", B=1, H=2, T=256, dk=128, dv=128, act="f32",
+                            chunk=chunk), repeat_key=True)
+    o, sf = _run(inp)
+    _check(inp, o, sf, 1e-3)

@@ -135,6 +135,54 @@ def _kda_form(q, k, v, la, beta, S0):
     return o, S
 
 
+def _prefix_states(q, k, v, la, b, w, S0):
+    """S_t after each token t = 1..T (the oracle run on every prefix)."""
+    T = q.shape[-2]
+    return [oracle.fwd(q[:, :t], k[:, :t], v[:, :t], la[:, :t], b[:, :t], w[:, :t], S0)[1]
+            for t in range(1, T + 1)]
+
+
+def test_full_erase_is_a_reflection():
+    """Expanded erase range ("Gated DeltaNet-2 Review" §5; sungsoo commentary):
+    with b = 2, no write, no decay and |k| = 1 the transition is the
+    reflection I - 2 k k^T, which has eigenvalue -1 along k.  So every step
+    keeps the Frobenius norm of the state and flips the sign of k_t^T S."""
+    q, k, v, la, b, w, S0 = _rand_case(T=9, dk=8, dv=5, seed=21)
+    two = np.full_like(b, 2.0)
+    Ss = _prefix_states(q, k, v, np.zeros_like(la), two, np.zeros_like(w), S0)
+    prev = S0
+    for t, St in enumerate(Ss):
+        np.testing.assert_allclose(np.linalg.norm(St, axis=(1, 2)), np.linalg.norm(S0, axis=(1, 2)),
+                                   rtol=1e-12)
+        kt = k[:, t]
+        np.testing.assert_allclose(np.einsum("bi,bij->bj", kt, St),
+                                   -np.einsum("bi,bij->bj", kt, prev), rtol=0, atol=1e-12)
+        prev = St
+
+
+def test_full_erase_twice_restores_the_state():
+    """The same key twice at b = 2 (no write, no decay) is a reflection
+    applied twice: the state comes back unchanged."""
+    q, k, v, la, b, w, S0 = _rand_case(T=6, dk=7, dv=4, seed=22)
+    k = np.repeat(k[:, :3], 2, axis=1)             # k1 k1 k2 k2 k3 k3
+    _, Sf = oracle.fwd(q, k, v, np.zeros_like(la), np.full_like(b, 2.0), np.zeros_like(w), S0)
+    np.testing.assert_allclose(Sf, S0, rtol=0, atol=1e-12)
+
+
+def test_erase_gates_up_to_two_never_grow_the_state():
+    """With |k| = 1, decay <= 1 and a per-token erase gate b in [0, 2] (the
+    same for every channel), the transition (I - b k k^T) D is a contraction
+    (eigenvalues 1 and 1 - b of the symmetric erase factor, times a decay of
+    at most 1), so with no write the state's norm never increases."""
+    q, k, v, la, b, w, S0 = _rand_case(T=16, dk=6, dv=5, seed=23, decay=0.5)
+    bt = rng0(24).random((b.shape[0], b.shape[1], 1)) * 2.0
+    Ss = _prefix_states(q, k, v, la, np.broadcast_to(bt, b.shape).copy(), np.zeros_like(w), S0)
+    norms = [np.linalg.norm(S0, axis=(1, 2))] + [np.linalg.norm(St, axis=(1, 2)) for St in Ss]
+    for a0, a1 in zip(norms, norms[1:]):
+        assert np.all(a1 <= a0 * (1 + 1e-12))
+    assert np.all(norms[-1] < norms[0] * 0.99)     # and it does shrink
+
+
 def test_tied_scalar_gates_give_gated_deltanet():
     q, k, v, la, b, w, S0 = _rand_case(T=16, dk=6, dv=5, seed=7)
     r = rng0(70)
