@@ -152,9 +152,11 @@ def bench_fwd(steps, warmup):
     return inp, wall_ms, ev_ms
 
 
-def bench_decode(steps, warmup, N=None):
+def bench_decode(steps, warmup, N=None, graph=False):
     """One decode step of N sequences x 32 heads (N defaults to the 256-sequence
-    workload; small N is the low-latency decode of a few sequences)."""
+    workload; small N is the low-latency decode of a few sequences).  graph:
+    the timed steps are captured once into a HIP graph and replayed (no launch
+    per step, as a serving loop runs them); the result is per step."""
     import torch
     import gdr_synth as gs
     import gated_delta_rule_24_amd as gdr
@@ -173,8 +175,19 @@ def bench_decode(steps, warmup, N=None):
         i[0] += 1
         gdr.gdr_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["b"], t["w"], S, o,
                             N, DH, DD, DD, 0)
-    wall_ms, ev_ms = time_loop(step, steps, warmup)
-    return wall_ms, ev_ms
+    if not graph:
+        wall_ms, ev_ms = time_loop(step, steps, warmup)
+        return wall_ms, ev_ms
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            step()
+    g.replay()
+    wall_ms, ev_ms = time_loop(g.replay, 5, 1)
+    return wall_ms / steps, ev_ms / steps
 
 
 def varlen_lengths():
@@ -362,9 +375,11 @@ def main():
     small = {}
     for n in SMALL_DECODE_N:
         _, ev = bench_decode(max(args.steps, 20), args.warmup, N=n)
+        _, evg = bench_decode(64, args.warmup, N=n, graph=True)
         small[f"N={n}"] = {"us_per_step": ev * 1e3,
+                           "us_per_step_graph": evg * 1e3,
                            "GB_per_s": n * DH * DEC_BYTES_PER_HEAD / (ev * 1e-3) / 1e9}
-        log(f"decode N={n}: {ev * 1e3:.1f} us/step")
+        log(f"decode N={n}: {ev * 1e3:.1f} us/step, {evg * 1e3:.1f} us/step replayed from a graph")
 
     lengths, var_wall, var_ev = bench_varlen(args.steps, args.warmup)
     var_bytes = VH * VT * FWD_BYTES_PER_TOKEN + len(lengths) * VH * FWD_STATE_BYTES_PER_HEAD
@@ -426,7 +441,9 @@ def main():
             "GB_per_s": dec_gbs,
             "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
             "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
-            "small_batch": {"workload": "decode H=32 d=128, N sequences (latency)", **small},
+            "small_batch": {"workload": "decode H=32 d=128, N sequences (latency); us_per_step: "
+                                        "back-to-back launches, us_per_step_graph: 64 steps "
+                                        "replayed from one HIP graph", **small},
         },
         "varlen_fwd": {
             "workload": (f"gdn2_chunk_fwd_varlen H={VH}, {VT} tokens per head packed as "

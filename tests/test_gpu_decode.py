@@ -102,3 +102,45 @@ def test_decode_full_workload_sampled():
         torch.cuda.synchronize()
         assert rel_err(o.cpu().numpy().reshape(N * H, d)[pick], o_ref) <= 2e-2
     assert rel_err(Sd.cpu().numpy().reshape(N * H, d, d)[pick], Sref) <= 2e-2
+
+
+def test_decode_steps_replay_from_a_graph():
+    """A run of decode steps captured into a graph (how a serving loop avoids
+    a launch per step at small batch) replays to the eager results, bit for
+    bit, on several replays with eager work between them."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    N, H, D, K = 2, 8, 128, 6
+    print(f"decode graph N={N} H={H} d={D} steps={K}", flush=True)
+    S_init = torch.from_numpy(gs.decode_state(N, H, D, D, seed=3)).cuda()
+    toks = []
+    for st in range(K):
+        t = gs.decode_token(N, H, D, D, st, seed=3)
+        toks.append({n: torch.from_numpy(a).to(torch.float32 if n == "log_alpha"
+                                               else torch.bfloat16).cuda() for n, a in t.items()})
+    outs = [torch.empty((N, H, D), dtype=torch.float32, device="cuda") for _ in range(K)]
+    S = S_init.clone()
+
+    def run():
+        for i, t in enumerate(toks):
+            gdr.gdr_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["b"], t["w"], S, outs[i],
+                                N, H, D, D, 0)
+    run()
+    torch.cuda.synchronize()
+    eager_o = [o.clone() for o in outs]
+    eager_S = S.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        S.copy_(S_init)
+        for o in outs:
+            o.zero_()
+        x = torch.randn(1 << 20, device="cuda")
+        x.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(S, eager_S), rep
+        for i in range(K):
+            assert torch.equal(outs[i], eager_o[i]), (rep, i)
