@@ -58,6 +58,13 @@ DEC_BYTES_PER_HEAD = 2 * DD * DD * 4 + (2 * DD * 2 + DD * 2 + DD * 4 + DD * 2 + 
 # sequences of 8192
 VH, VT, VMEAN = 16, 16384, 1024
 
+# token-mixer prologue / epilogue on the forward workload's shape; algorithmic
+# HBM bytes per head-token (channel gates): the prologue reads q, k, v, b, w
+# logits (bf16) and the log-decay logits (fp32) and writes the same shapes;
+# the epilogue reads o (fp32) and the output-gate logits (bf16), writes y (bf16)
+MIX_PRO_BYTES_PER_TOKEN = 2 * (3 * FD * 2 + FD * 4 + 2 * FD * 2)
+MIX_EPI_BYTES_PER_TOKEN = FD * 4 + FD * 2 + FD * 2
+
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
 # head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
 # d log-decay, db, dv, dw fp32; plus S0 read and dS0 written per head
@@ -262,6 +269,33 @@ def bench_bwd_varlen(steps, warmup):
     return lengths, wall_ms, ev_ms
 
 
+def bench_mixer(steps, warmup):
+    """Token-mixer prologue and epilogue at B=2, H=16, T=8192, d=128 (channel
+    gates), each timed on its own; returns event ms per call of each."""
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    m = gs.mixer_inputs(FB, FH, FT, FD, FD, seed=0)
+    d = {n: torch.from_numpy(a).to(torch.float32 if n in ("conv_q", "conv_k", "conv_v", "a_pre",
+                                                         "norm_weight") else torch.bfloat16).cuda()
+         for n, a in m.items()}
+    out = {n: torch.empty_like(d[src]) for n, src in (("q", "q_pre"), ("k", "k_pre"), ("v", "v_pre"),
+                                                      ("la", "a_pre"), ("b", "b_pre"), ("w", "w_pre"))}
+    o = torch.randn((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
+    y = torch.empty((FB, FH, FT, FD), dtype=torch.bfloat16, device="cuda")
+
+    def pro():
+        gdr.gdr_mixer_prologue(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], d["a_pre"], d["b_pre"], d["w_pre"], out["q"], out["k"],
+                               out["v"], out["la"], out["b"], out["w"], FB, FH, FT, FD, FD, 0)
+
+    def epi():
+        gdr.gdr_mixer_epilogue(o, d["g"], d["norm_weight"], y, FB, FH, FT, FD, 0)
+    _, pro_ms = time_loop(pro, steps, warmup)
+    _, epi_ms = time_loop(epi, steps, warmup)
+    return pro_ms, epi_ms
+
+
 def bench_copy(steps, warmup):
     """Plain 1 GiB device copy, the calibration kernel for HBM counters."""
     import torch
@@ -320,7 +354,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen", "bwd_varlen"],
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen", "bwd_varlen", "mixer"],
                     default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -354,6 +388,10 @@ def main():
         w, e, _ = bench_bwd(args.steps, args.warmup)
         log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
         return
+    if args.only == "mixer":
+        pm, em = bench_mixer(args.steps, args.warmup)
+        log(f"mixer prologue {pm * 1e3:.1f} us, epilogue {em * 1e3:.1f} us")
+        return
     if args.only == "bwd_varlen":
         lengths, w, e = bench_bwd_varlen(args.steps, args.warmup)
         log(f"bwd varlen ({len(lengths)} sequences): {e * 1e3:.1f} us/step")
@@ -386,6 +424,13 @@ def main():
     var_gbs = var_bytes / (var_ev * 1e-3) / 1e9
     log(f"varlen fwd ({len(lengths)} sequences, longest {max(lengths)}): "
         f"{var_ev * 1e3:.1f} us/step, {var_gbs:.0f} GB/s")
+
+    mix_pro_ms, mix_epi_ms = bench_mixer(args.steps, args.warmup)
+    ntok_mix = FB * FH * FT
+    mix_pro_gbs = ntok_mix * MIX_PRO_BYTES_PER_TOKEN / (mix_pro_ms * 1e-3) / 1e9
+    mix_epi_gbs = ntok_mix * MIX_EPI_BYTES_PER_TOKEN / (mix_epi_ms * 1e-3) / 1e9
+    log(f"mixer: prologue {mix_pro_ms * 1e3:.1f} us ({mix_pro_gbs:.0f} GB/s), "
+        f"epilogue {mix_epi_ms * 1e3:.1f} us ({mix_epi_gbs:.0f} GB/s)")
 
     bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
     bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
@@ -456,6 +501,17 @@ def main():
             "GB_per_s": var_gbs,
             "frac_hbm_peak": var_gbs / HBM_PEAK_GBS,
             "bytes_per_step": var_bytes,
+        },
+        "mixer": {
+            "workload": "token-mixer prologue (conv+SiLU+L2 norm of q, k; conv+SiLU of v; "
+                        "gates) and epilogue (RMS norm x SiLU gate) at B=2 H=16 T=8192 d=128",
+            "prologue_us": mix_pro_ms * 1e3,
+            "prologue_GB_per_s": mix_pro_gbs,
+            "prologue_frac_hbm_peak": mix_pro_gbs / HBM_PEAK_GBS,
+            "epilogue_us": mix_epi_ms * 1e3,
+            "epilogue_GB_per_s": mix_epi_gbs,
+            "epilogue_frac_hbm_peak": mix_epi_gbs / HBM_PEAK_GBS,
+            "bytes_per_head_token": [MIX_PRO_BYTES_PER_TOKEN, MIX_EPI_BYTES_PER_TOKEN],
         },
         "backward": {
             "workload": "gdn2_chunk_bwd B=1 H=32 T=16384 d_k=d_v=128 chunk=64, dO only",

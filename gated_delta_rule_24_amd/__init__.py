@@ -79,6 +79,10 @@ def _load():
         lib.gdr_chunk_bwd_varlen_workspace_bytes.restype = S
         lib.gdr_chunk_bwd_varlen.argtypes = [P] * 17 + [I] * 5 + [U, P, S, P]
         lib.gdr_chunk_bwd_varlen.restype = I
+        lib.gdr_mixer_prologue.argtypes = [P] * 15 + [I] * 5 + [U, P]
+        lib.gdr_mixer_prologue.restype = I
+        lib.gdr_mixer_epilogue.argtypes = [P] * 4 + [I] * 4 + [U, P]
+        lib.gdr_mixer_epilogue.restype = I
         _lib = lib
     return _lib
 
@@ -91,7 +95,8 @@ def lib():
 EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
                     "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
                     "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
-                    "gdr_chunk_bwd_varlen_workspace_bytes", "gdr_chunk_bwd_varlen")
+                    "gdr_chunk_bwd_varlen_workspace_bytes", "gdr_chunk_bwd_varlen",
+                    "gdr_mixer_prologue", "gdr_mixer_epilogue")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -198,6 +203,21 @@ def gdr_chunk_bwd_varlen(q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv,
                                       _ptr(dS0), _ptr(cu_seqlens), nseq, H, T, d_k, d_v, flags,
                                       _ptr(workspace), workspace_bytes, _stream(stream))
     _check("gdr_chunk_bwd_varlen", st)
+
+
+def gdr_mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, q, k, v,
+                       log_alpha, b, w, B, H, T, d_k, d_v, flags, stream=None):
+    st = _load().gdr_mixer_prologue(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_q),
+                                    _ptr(conv_k), _ptr(conv_v), _ptr(a_pre), _ptr(b_pre),
+                                    _ptr(w_pre), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                    _ptr(b), _ptr(w), B, H, T, d_k, d_v, flags, _stream(stream))
+    _check("gdr_mixer_prologue", st)
+
+
+def gdr_mixer_epilogue(o, g, norm_weight, y, B, H, T, d_v, flags=0, stream=None):
+    st = _load().gdr_mixer_epilogue(_ptr(o), _ptr(g), _ptr(norm_weight), _ptr(y), B, H, T, d_v,
+                                    flags, _stream(stream))
+    _check("gdr_mixer_epilogue", st)
 
 
 # ---------------------------------------------------------------------------
@@ -323,3 +343,33 @@ def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None
                          out["dv"], out["dlog_alpha"], out["db"], out["dw"], out["dS0"],
                          cu_seqlens, nseq, H, T, dk, dv, flags, ws, nbytes, stream)
     return out
+
+
+def mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, stream=None):
+    """[B,H,T,d] bf16 projection outputs (a_pre fp32; gate logits [B,H,T,d]
+    or [B,H,T]) and fp32 [H,d,4] convolution taps -> dict q, k, v, log_alpha,
+    b, w: the inputs of chunk_fwd."""
+    B, H, T, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    flags = 0
+    if a_pre.dim() == 3:
+        flags |= GDR_ALPHA_SCALAR
+    if b_pre.dim() == 3:
+        flags |= GDR_B_SCALAR
+    if w_pre.dim() == 3:
+        flags |= GDR_W_SCALAR
+    out = dict(q=torch.empty_like(q_pre), k=torch.empty_like(k_pre), v=torch.empty_like(v_pre),
+               log_alpha=torch.empty_like(a_pre), b=torch.empty_like(b_pre),
+               w=torch.empty_like(w_pre))
+    gdr_mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, out["q"],
+                       out["k"], out["v"], out["log_alpha"], out["b"], out["w"], B, H, T, dk, dv,
+                       flags, stream)
+    return out
+
+
+def mixer_epilogue(o, g, norm_weight, stream=None):
+    """o fp32 [B,H,T,dv], g bf16 [B,H,T,dv], norm_weight fp32 [dv] -> y bf16."""
+    B, H, T, dv = o.shape
+    y = torch.empty(o.shape, dtype=torch.bfloat16, device=o.device)
+    gdr_mixer_epilogue(o, g, norm_weight, y, B, H, T, dv, 0, stream)
+    return y

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgdr.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_fwd_wy.hip", "gdr_bwd_wy.hip",
+SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_fwd_wy.hip", "gdr_bwd_wy.hip", "gdr_mixer.hip",
            "gdr_bwd.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

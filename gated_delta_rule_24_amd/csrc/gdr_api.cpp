@@ -248,4 +248,52 @@ gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
     return from_hip(gdr::launch_bwd_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
+gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* v_pre,
+                              const float* conv_q, const float* conv_k, const float* conv_v,
+                              const float* a_pre, const void* b_pre, const void* w_pre, void* q,
+                              void* k, void* v, float* log_alpha, void* b, void* w, int B, int H,
+                              int T, int d_k, int d_v, uint32_t flags, void* stream) {
+    const uint32_t gate_modes = GDR_ALPHA_SCALAR | GDR_B_SCALAR | GDR_W_SCALAR;
+    if (flags & ~(kKnownFlags & ~GDR_OUT_BF16 & ~GDR_FWD_GENERIC)) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * ((T + 63) / 64) > (1LL << 31) - 1)
+        return GDR_ERR_INVALID_ARG;
+    if (!gdr::mixer_supported(d_k) || !gdr::mixer_supported(d_v) || (flags & ~gate_modes))
+        return GDR_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre,
+                          q, k, v, log_alpha, b, w};
+    for (const void* ptr : ptrs) {
+        if (T > 0 && !ptr) return GDR_ERR_INVALID_ARG;
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    }
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+    gdr::MixerParams p;
+    p.q_pre = q_pre; p.k_pre = k_pre; p.v_pre = v_pre;
+    p.conv_q = conv_q; p.conv_k = conv_k; p.conv_v = conv_v;
+    p.a_pre = a_pre; p.b_pre = b_pre; p.w_pre = w_pre;
+    p.q = q; p.k = k; p.v = v; p.la = log_alpha; p.b = b; p.w = w;
+    p.BH = B * H; p.H = H; p.T = T; p.flags = flags;
+    return from_hip(gdr::launch_mixer_prologue(p, d_k, d_v, (hipStream_t)stream));
+}
+
+gdr_status gdr_mixer_epilogue(const float* o, const void* g, const float* norm_weight, void* y,
+                              int B, int H, int T, int d_v, uint32_t flags, void* stream) {
+    if (flags != 0) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * T > (1LL << 40)) return GDR_ERR_INVALID_ARG;
+    if (!gdr::mixer_supported(d_v)) return GDR_ERR_UNSUPPORTED;
+    const void* ptrs[] = {o, g, norm_weight, y};
+    for (const void* ptr : ptrs) {
+        if (T > 0 && !ptr) return GDR_ERR_INVALID_ARG;
+        if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    }
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+    gdr::EpilogueParams p;
+    p.o = o; p.g = g; p.norm_weight = norm_weight; p.y = y;
+    p.rows = (long long)B * H * T;
+    return from_hip(gdr::launch_mixer_epilogue(p, d_v, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -133,4 +133,38 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
 size_t bwd_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
 hipError_t launch_bwd_varlen(const BwdParams& p, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st);
 
+// Token-mixer prologue and epilogue (bf16 streams, d in {64, 128}).
+constexpr int kConvTaps = 4;   // causal convolution taps per channel
+struct MixerParams {
+    const void* q_pre;     // [BH, T, DK] bf16 projection outputs
+    const void* k_pre;
+    const void* v_pre;     // [BH, T, DV]
+    const float* conv_q;   // [H, DK, kConvTaps] fp32; tap j weights token t - j
+    const float* conv_k;
+    const float* conv_v;   // [H, DV, kConvTaps]
+    const float* a_pre;    // log-decay logits, fp32 [BH, T, DK] or [BH, T]
+    const void* b_pre;     // erase-gate logits, bf16 [BH, T, DK] or [BH, T]
+    const void* w_pre;     // write-gate logits, bf16 [BH, T, DV] or [BH, T]
+    void* q;               // outputs: bf16 q, k [BH, T, DK], v [BH, T, DV]
+    void* k;
+    void* v;
+    float* la;             // fp32 log alpha, shaped as a_pre
+    void* b;               // bf16 gates, shaped as b_pre / w_pre
+    void* w;
+    int BH;
+    int H;
+    int T;
+    uint32_t flags;        // GDR_ALPHA_SCALAR, GDR_B_SCALAR, GDR_W_SCALAR
+};
+struct EpilogueParams {
+    const float* o;        // [rows, DV] fp32 recurrence output
+    const void* g;         // [rows, DV] bf16 output-gate logits
+    const float* norm_weight;  // [DV] fp32
+    void* y;               // [rows, DV] bf16
+    long long rows;        // B * H * T
+};
+bool mixer_supported(int d);
+hipError_t launch_mixer_prologue(const MixerParams& p, int dk, int dv, hipStream_t st);
+hipError_t launch_mixer_epilogue(const EpilogueParams& p, int dv, hipStream_t st);
+
 }  // namespace gdr

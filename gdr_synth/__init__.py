@@ -192,6 +192,29 @@ def packed_inputs(lengths, H: int, dk: int, dv: int, seed: int = 0,
     return inp
 
 
+def mixer_inputs(B: int, H: int, T: int, dk: int, dv: int, *, alpha_mode: str = "channel",
+                 b_mode: str = "channel", w_mode: str = "channel", seed: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of the token-mixer prologue and epilogue: the projections'
+    outputs q_pre, k_pre, v_pre ~ N(0, 1) (bf16 values), depthwise causal
+    convolution taps [H, d, 4] ~ N(0, 1/4) (fp32), decay logits a_pre ~
+    N(4, 1) (fp32; alpha = sigmoid(a_pre) is about 0.98, so a chunk of 64
+    tokens decays by about 1 nat), erase/write gate logits ~ N(0, 1), the
+    output-gate logits g ~ N(0, 1) and the RMS-norm weight 1 + N(0, 0.01)."""
+    rng = np.random.default_rng([seed, 13])
+    n = lambda *shape: rng.standard_normal(shape, dtype=np.float32)
+    ash = (B, H, T, dk) if alpha_mode == "channel" else (B, H, T)
+    bsh = (B, H, T, dk) if b_mode == "channel" else (B, H, T)
+    wsh = (B, H, T, dv) if w_mode == "channel" else (B, H, T)
+    return dict(q_pre=bf16_round(n(B, H, T, dk)), k_pre=bf16_round(n(B, H, T, dk)),
+                v_pre=bf16_round(n(B, H, T, dv)),
+                conv_q=n(H, dk, 4) * np.float32(0.5), conv_k=n(H, dk, 4) * np.float32(0.5),
+                conv_v=n(H, dv, 4) * np.float32(0.5),
+                a_pre=(n(*ash) + np.float32(4.0)).astype(np.float32),
+                b_pre=bf16_round(n(*bsh)), w_pre=bf16_round(n(*wsh)),
+                g=bf16_round(n(B, H, T, dv)),
+                norm_weight=(np.float32(1.0) + n(dv) * np.float32(0.1)).astype(np.float32))
+
+
 def packed_lengths(n: int, mean: int, seed: int = 0, lo: int = 1) -> list:
     """n sequence lengths with a long-tailed mix (geometric around mean,
     at least lo), as packed training batches of documents have."""

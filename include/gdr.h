@@ -254,6 +254,54 @@ gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v,
                                 int d_k, int d_v, uint32_t flags, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * Token-mixer prologue: the element-wise and short-window steps between the
+ * caller's linear projections and the recurrence ("Gated DeltaNet study
+ * notes" §2 token mixer block design; "Gated DeltaNet-2 Review" §4-3
+ * engineering notes), in one pass:
+ *   q = L2norm(SiLU(conv(q_pre))),  k = L2norm(SiLU(conv(k_pre))),
+ *   v = SiLU(conv(v_pre)),  log_alpha = log(sigmoid(a_pre)) in fp32,
+ *   b = sigmoid(b_pre),  w = sigmoid(w_pre).
+ * conv is the depthwise causal convolution with 4 taps per channel, zero
+ * before the first token of each sequence; L2norm(x) = x / sqrt(sum x^2 +
+ * 1e-6) over the head's d_k channels.  All arithmetic is fp32.
+ *
+ *   q_pre, k_pre : bf16 [B, H, T, d_k]   v_pre : bf16 [B, H, T, d_v]
+ *   conv_q, conv_k : fp32 [H, d_k, 4]    conv_v : fp32 [H, d_v, 4]
+ *                  taps of channel c of head h: element j weights token t - j
+ *   a_pre  : fp32 [B, H, T, d_k] (or [B, H, T] with GDR_ALPHA_SCALAR)
+ *   b_pre  : bf16 [B, H, T, d_k] (or [B, H, T] with GDR_B_SCALAR)
+ *   w_pre  : bf16 [B, H, T, d_v] (or [B, H, T] with GDR_W_SCALAR)
+ *   outputs, written: q, k, v bf16 in the shapes of q_pre, k_pre, v_pre;
+ *   log_alpha fp32 shaped as a_pre; b, w bf16 shaped as b_pre, w_pre.  These
+ *   are exactly the inputs gdr_chunk_fwd takes with the same gate flags.
+ * Outputs must not alias inputs.  Flags: the three gate modes only.
+ * Supported: d_k, d_v in {64, 128}; GDR_ERR_UNSUPPORTED otherwise (also for
+ * GDR_ACT_F32).
+ */
+gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* v_pre,
+                              const float* conv_q, const float* conv_k, const float* conv_v,
+                              const float* a_pre, const void* b_pre, const void* w_pre,
+                              void* q, void* k, void* v, float* log_alpha, void* b, void* w,
+                              int B, int H, int T, int d_k, int d_v, uint32_t flags,
+                              void* stream);
+
+/*
+ * Token-mixer epilogue: the recurrent output RMS-normalised and gated before
+ * the caller's output projection ("Gated DeltaNet-2 Review" §4-3), per
+ * (token, head):
+ *   y = o / sqrt(mean(o^2) + 1e-6) * norm_weight * SiLU(g)
+ * with the mean over the head's d_v channels, in fp32.
+ *
+ *   o           : fp32 [B, H, T, d_v] (gdr_chunk_fwd's output)
+ *   g           : bf16 [B, H, T, d_v] output-gate logits
+ *   norm_weight : fp32 [d_v], shared by the heads
+ *   y           : bf16 [B, H, T, d_v], written; must not alias o or g
+ * flags must be 0.  Supported: d_v in {64, 128}.
+ */
+gdr_status gdr_mixer_epilogue(const float* o, const void* g, const float* norm_weight, void* y,
+                              int B, int H, int T, int d_v, uint32_t flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

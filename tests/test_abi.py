@@ -206,3 +206,27 @@ def test_bwd_varlen_workspace_query():
     assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 64, 0) == 0
     assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0
     assert lib.gdr_chunk_bwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
+
+
+def test_mixer_argument_validation():
+    lib = _lib()
+
+    def pro(**kw):
+        a = dict(ptrs=[A] * 15, B=1, H=2, T=64, dk=128, dv=128, flags=0)
+        a.update(kw)
+        return lib.gdr_mixer_prologue(*a["ptrs"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                      a["flags"], None)
+
+    def epi(**kw):
+        a = dict(ptrs=[A] * 4, B=1, H=2, T=64, dv=128, flags=0)
+        a.update(kw)
+        return lib.gdr_mixer_epilogue(*a["ptrs"], a["B"], a["H"], a["T"], a["dv"], a["flags"], None)
+    assert pro(ptrs=[A] * 14 + [None]) == 1          # w output missing
+    assert pro(ptrs=[MIS] + [A] * 14) == 1
+    assert pro(B=0) == 1 and pro(T=-1) == 1
+    assert pro(flags=0x2) == 1 and pro(flags=0x20) == 1
+    assert pro(flags=0x1) == 2                       # fp32 activations: no kernel
+    assert pro(dk=32) == 2 and pro(dv=96) == 2
+    assert epi(ptrs=[A, A, None, A]) == 1
+    assert epi(flags=0x4) == 1 and epi(H=0) == 1
+    assert epi(dv=16) == 2
