@@ -64,6 +64,9 @@ VH, VT, VMEAN = 16, 16384, 1024
 # the epilogue reads o (fp32) and the output-gate logits (bf16), writes y (bf16)
 MIX_PRO_BYTES_PER_TOKEN = 2 * (3 * FD * 2 + FD * 4 + 2 * FD * 2)
 MIX_EPI_BYTES_PER_TOKEN = FD * 4 + FD * 2 + FD * 2
+# with the gating fused into the recurrence's loads (GDR_GATE_LOGITS) the
+# prologue reads and writes q, k, v only
+MIX_QKV_BYTES_PER_TOKEN = 2 * 3 * FD * 2
 
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
 # head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
@@ -291,9 +294,26 @@ def bench_mixer(steps, warmup):
 
     def epi():
         gdr.gdr_mixer_epilogue(o, d["g"], d["norm_weight"], y, FB, FH, FT, FD, 0)
+
+    def qkv():
+        gdr.gdr_mixer_prologue(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], None, None, None, out["q"], out["k"], out["v"], None, None,
+                               None, FB, FH, FT, FD, FD, gdr.GDR_GATE_LOGITS)
+    # the forward taking the gate logits straight from the projections
+    S0 = torch.zeros((FB, FH, FD, FD), dtype=torch.float32, device="cuda")
+    of = torch.empty((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
+    fl = gdr.GDR_GATE_LOGITS
+    nb = gdr.gdr_chunk_fwd_workspace_bytes(FB, FH, FT, FD, FD, FC, fl)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def fwd_logits():
+        gdr.gdr_chunk_fwd(out["q"], out["k"], out["v"], d["a_pre"], d["b_pre"], d["w_pre"], S0, of, None,
+                          FB, FH, FT, FD, FD, FC, fl, ws, nb)
     _, pro_ms = time_loop(pro, steps, warmup)
     _, epi_ms = time_loop(epi, steps, warmup)
-    return pro_ms, epi_ms
+    _, qkv_ms = time_loop(qkv, steps, warmup)
+    _, fl_ms = time_loop(fwd_logits, steps, warmup)
+    return pro_ms, epi_ms, qkv_ms, fl_ms
 
 
 def bench_copy(steps, warmup):
@@ -389,8 +409,9 @@ def main():
         log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
         return
     if args.only == "mixer":
-        pm, em = bench_mixer(args.steps, args.warmup)
-        log(f"mixer prologue {pm * 1e3:.1f} us, epilogue {em * 1e3:.1f} us")
+        pm, em, qm, fm = bench_mixer(args.steps, args.warmup)
+        log(f"mixer prologue {pm * 1e3:.1f} us, epilogue {em * 1e3:.1f} us, q/k/v-only prologue "
+            f"{qm * 1e3:.1f} us, forward on gate logits {fm * 1e3:.1f} us")
         return
     if args.only == "bwd_varlen":
         lengths, w, e = bench_bwd_varlen(args.steps, args.warmup)
@@ -425,7 +446,7 @@ def main():
     log(f"varlen fwd ({len(lengths)} sequences, longest {max(lengths)}): "
         f"{var_ev * 1e3:.1f} us/step, {var_gbs:.0f} GB/s")
 
-    mix_pro_ms, mix_epi_ms = bench_mixer(args.steps, args.warmup)
+    mix_pro_ms, mix_epi_ms, mix_qkv_ms, mix_fl_ms = bench_mixer(args.steps, args.warmup)
     ntok_mix = FB * FH * FT
     mix_pro_gbs = ntok_mix * MIX_PRO_BYTES_PER_TOKEN / (mix_pro_ms * 1e-3) / 1e9
     mix_epi_gbs = ntok_mix * MIX_EPI_BYTES_PER_TOKEN / (mix_epi_ms * 1e-3) / 1e9
@@ -512,6 +533,15 @@ def main():
             "epilogue_GB_per_s": mix_epi_gbs,
             "epilogue_frac_hbm_peak": mix_epi_gbs / HBM_PEAK_GBS,
             "bytes_per_head_token": [MIX_PRO_BYTES_PER_TOKEN, MIX_EPI_BYTES_PER_TOKEN],
+            "gating_fused": {
+                "what": "prologue producing q, k, v only; the forward reading the gate logits "
+                        "(GDR_GATE_LOGITS)",
+                "prologue_qkv_us": mix_qkv_ms * 1e3,
+                "prologue_qkv_GB_per_s": ntok_mix * MIX_QKV_BYTES_PER_TOKEN / (mix_qkv_ms * 1e-3) / 1e9,
+                "fwd_on_logits_us": mix_fl_ms * 1e3,
+                "block_us": (mix_qkv_ms + mix_fl_ms + mix_epi_ms) * 1e3,
+                "block_us_unfused": (mix_pro_ms + ev_ms + mix_epi_ms) * 1e3,
+            },
         },
         "backward": {
             "workload": "gdn2_chunk_bwd B=1 H=32 T=16384 d_k=d_v=128 chunk=64, dO only",

@@ -36,6 +36,7 @@ GDR_ALPHA_SCALAR = 0x4
 GDR_B_SCALAR = 0x8
 GDR_W_SCALAR = 0x10
 GDR_FWD_GENERIC = 0x20
+GDR_GATE_LOGITS = 0x40
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "launch", 5: "device"}
 
@@ -122,9 +123,10 @@ def _act_flag(t: torch.Tensor) -> int:
     raise ValueError(f"activation dtype must be bfloat16 or float32, got {t.dtype}")
 
 
-def gate_flags(q, log_alpha, b, w) -> int:
-    """Flags for the dtype and gate modes implied by tensor ranks."""
-    f = _act_flag(q)
+def gate_flags(q, log_alpha, b, w, gate_logits: bool = False) -> int:
+    """Flags for the dtype and gate modes implied by tensor ranks (gate_logits:
+    log_alpha, b and w hold logits, see GDR_GATE_LOGITS)."""
+    f = _act_flag(q) | (GDR_GATE_LOGITS if gate_logits else 0)
     if log_alpha.dim() == q.dim() - 1:
         f |= GDR_ALPHA_SCALAR
     if b.dim() == q.dim() - 1:
@@ -227,7 +229,7 @@ def gdr_mixer_epilogue(o, g, norm_weight, y, B, H, T, d_v, flags=0, stream=None)
 
 def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
               out_dtype=torch.float32, return_state: bool = True, stream=None,
-              generic: bool = False, path: str = "auto"):
+              generic: bool = False, path: str = "auto", gate_logits: bool = False):
     """q, k: [B,H,T,dk]; v: [B,H,T,dv]; log_alpha, b: [B,H,T,dk] or [B,H,T];
     w: [B,H,T,dv] or [B,H,T]; S0: [B,H,dk,dv] fp32 or None.
     path "auto" passes a workspace (two-pass kernels where they apply),
@@ -235,7 +237,7 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
     Returns (o [B,H,T,dv], S_final [B,H,dk,dv] or None)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    flags = gate_flags(q, log_alpha, b, w)
+    flags = gate_flags(q, log_alpha, b, w, gate_logits)
     if out_dtype == torch.bfloat16:
         flags |= GDR_OUT_BF16
     if generic:
@@ -255,7 +257,7 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
 
 
 def chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, out_dtype=torch.float32,
-                     return_state: bool = True, stream=None):
+                     return_state: bool = True, stream=None, gate_logits: bool = False):
     """Packed sequences: q, k: [H,T,dk]; v: [H,T,dv]; log_alpha, b: [H,T,dk] or
     [H,T]; w: [H,T,dv] or [H,T]; cu_seqlens: int32 [nseq+1] on the GPU; S0:
     [nseq,H,dk,dv] fp32 or None.  Returns (o [H,T,dv], S_final [nseq,H,dk,dv] or None)."""
@@ -264,7 +266,7 @@ def chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, out_dtype=to
     if cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     nseq = cu_seqlens.numel() - 1
-    flags = gate_flags(q, log_alpha, b, w)
+    flags = gate_flags(q, log_alpha, b, w, gate_logits)
     if out_dtype == torch.bfloat16:
         flags |= GDR_OUT_BF16
     o = torch.empty((H, T, dv), dtype=out_dtype, device=q.device)
@@ -278,12 +280,13 @@ def chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, out_dtype=to
     return o, Sf
 
 
-def decode_step(q, k, v, log_alpha, b, w, S, out_dtype=torch.float32, o=None, stream=None):
+def decode_step(q, k, v, log_alpha, b, w, S, out_dtype=torch.float32, o=None, stream=None,
+                gate_logits: bool = False):
     """One token per (n, h): q, k: [N,H,dk]; v: [N,H,dv]; gates channel or
     scalar ([N,H]); S: [N,H,dk,dv] fp32, updated in place.  Returns o."""
     N, H, dk = q.shape
     dv = v.shape[-1]
-    flags = gate_flags(q, log_alpha, b, w)
+    flags = gate_flags(q, log_alpha, b, w, gate_logits)
     if out_dtype == torch.bfloat16:
         flags |= GDR_OUT_BF16
     if o is None:
@@ -292,13 +295,14 @@ def decode_step(q, k, v, log_alpha, b, w, S, out_dtype=torch.float32, o=None, st
     return o
 
 
-def chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, chunk: int = 64, stream=None):
+def chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, chunk: int = 64, stream=None,
+              gate_logits: bool = False):
     """Gradients of L = <dO, o> + <dS_final, S_final>.  Returns a dict of fp32
     tensors dq, dk, dv, dlog_alpha, db, dw (scalar gates keep their scalar
     shape) and dS0."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    flags = gate_flags(q, log_alpha, b, w)
+    flags = gate_flags(q, log_alpha, b, w, gate_logits)
     dev = q.device
     f32 = torch.float32
     out = dict(dq=torch.empty((B, H, T, dk), dtype=f32, device=dev),
@@ -316,7 +320,8 @@ def chunk_bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, chunk: int = 64, 
     return out
 
 
-def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None, stream=None):
+def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None, stream=None,
+                     gate_logits: bool = False):
     """Packed sequences ([H,T,...] streams, cu_seqlens int32 on the GPU): the
     gradients of L = <dO, o> + <dS_final, S_final> as a dict of fp32 tensors
     dq, dk, dv, dlog_alpha, db, dw (in the inputs' shapes) and dS0 [nseq,H,dk,dv]."""
@@ -325,7 +330,7 @@ def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None
     if cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     nseq = cu_seqlens.numel() - 1
-    flags = gate_flags(q, log_alpha, b, w)
+    flags = gate_flags(q, log_alpha, b, w, gate_logits)
     dev = q.device
     f32 = torch.float32
     out = dict(dq=torch.empty((H, T, dk), dtype=f32, device=dev),
@@ -345,22 +350,29 @@ def chunk_bwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0, dO, dS_final=None
     return out
 
 
-def mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, stream=None):
+def mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, stream=None,
+                   gate_logits: bool = False):
     """[B,H,T,d] bf16 projection outputs (a_pre fp32; gate logits [B,H,T,d]
     or [B,H,T]) and fp32 [H,d,4] convolution taps -> dict q, k, v, log_alpha,
-    b, w: the inputs of chunk_fwd."""
+    b, w: the inputs of chunk_fwd.  gate_logits: only q, k, v are produced;
+    log_alpha, b and w are the logits themselves, for the recurrence calls
+    made with gate_logits=True."""
     B, H, T, dk = q_pre.shape
     dv = v_pre.shape[-1]
-    flags = 0
+    flags = GDR_GATE_LOGITS if gate_logits else 0
     if a_pre.dim() == 3:
         flags |= GDR_ALPHA_SCALAR
     if b_pre.dim() == 3:
         flags |= GDR_B_SCALAR
     if w_pre.dim() == 3:
         flags |= GDR_W_SCALAR
-    out = dict(q=torch.empty_like(q_pre), k=torch.empty_like(k_pre), v=torch.empty_like(v_pre),
-               log_alpha=torch.empty_like(a_pre), b=torch.empty_like(b_pre),
-               w=torch.empty_like(w_pre))
+    out = dict(q=torch.empty_like(q_pre), k=torch.empty_like(k_pre), v=torch.empty_like(v_pre))
+    if gate_logits:
+        gdr_mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, None, None, None, out["q"],
+                           out["k"], out["v"], None, None, None, B, H, T, dk, dv, flags, stream)
+        out.update(log_alpha=a_pre, b=b_pre, w=w_pre)
+        return out
+    out.update(log_alpha=torch.empty_like(a_pre), b=torch.empty_like(b_pre), w=torch.empty_like(w_pre))
     gdr_mixer_prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre, out["q"],
                        out["k"], out["v"], out["log_alpha"], out["b"], out["w"], B, H, T, dk, dv,
                        flags, stream)

@@ -10,7 +10,7 @@
 namespace {
 
 constexpr uint32_t kKnownFlags = GDR_ACT_F32 | GDR_OUT_BF16 | GDR_ALPHA_SCALAR | GDR_B_SCALAR |
-                                 GDR_W_SCALAR | GDR_FWD_GENERIC;
+                                 GDR_W_SCALAR | GDR_FWD_GENERIC | GDR_GATE_LOGITS;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -82,6 +82,7 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const size_t need = gdr_chunk_fwd_workspace_bytes(B, H, T, d_k, d_v, chunk, flags);
     const bool two_pass = workspace != nullptr && need > 0;
     if (two_pass && workspace_bytes < need) return GDR_ERR_WORKSPACE;
+    if ((flags & GDR_GATE_LOGITS) && T > 0 && !two_pass) return GDR_ERR_UNSUPPORTED;
     gdr_status ds = check_device();
     if (ds != GDR_OK) return ds;
 
@@ -178,6 +179,8 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
     if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
+    if ((flags & GDR_GATE_LOGITS) && T > 0 && !gdr::fwd_wy_supported(d_k, d_v, chunk, flags))
+        return GDR_ERR_UNSUPPORTED;
     const size_t need = gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
     gdr_status ds = check_device();
@@ -253,17 +256,21 @@ gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* 
                               const float* a_pre, const void* b_pre, const void* w_pre, void* q,
                               void* k, void* v, float* log_alpha, void* b, void* w, int B, int H,
                               int T, int d_k, int d_v, uint32_t flags, void* stream) {
-    const uint32_t gate_modes = GDR_ALPHA_SCALAR | GDR_B_SCALAR | GDR_W_SCALAR;
+    const uint32_t gate_modes = GDR_ALPHA_SCALAR | GDR_B_SCALAR | GDR_W_SCALAR | GDR_GATE_LOGITS;
     if (flags & ~(kKnownFlags & ~GDR_OUT_BF16 & ~GDR_FWD_GENERIC)) return GDR_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
     if ((long long)B * H > (1LL << 28) || (long long)B * H * ((T + 63) / 64) > (1LL << 31) - 1)
         return GDR_ERR_INVALID_ARG;
     if (!gdr::mixer_supported(d_k) || !gdr::mixer_supported(d_v) || (flags & ~gate_modes))
         return GDR_ERR_UNSUPPORTED;
-    const void* ptrs[] = {q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre,
-                          q, k, v, log_alpha, b, w};
-    for (const void* ptr : ptrs) {
-        if (T > 0 && !ptr) return GDR_ERR_INVALID_ARG;
+    // with GDR_GATE_LOGITS the gates stay logits for the recurrence to take:
+    // only q, k and v are produced and the gate pointers are not used
+    const bool gates = !(flags & GDR_GATE_LOGITS);
+    const void* ptrs[] = {q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, q, k, v,
+                          a_pre, b_pre, w_pre, log_alpha, b, w};
+    for (int i = 0; i < 15; ++i) {
+        const void* ptr = ptrs[i];
+        if (T > 0 && !ptr && (i < 9 || gates)) return GDR_ERR_INVALID_ARG;
         if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
     }
     gdr_status ds = check_device();

@@ -426,6 +426,16 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         return *reinterpret_cast<const half8*>(base + off + lo16);
     };
     const float poison = *reinterpret_cast<const int*>(rec + R::G + D * 4) ? __builtin_nanf("") : 0.f;
+    // gates given as logits: the values are sigmoid / log sigmoid of the inputs,
+    // the gate gradients are those of the logits (absent tokens: decay logit +inf)
+    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    auto gate4 = [&](floatx4 x) __attribute__((always_inline)) {
+        if (lg) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = gate_sigmoid(x[i]);
+        }
+        return x;
+    };
 
     // ================= phase A: value columns 16 vt .. 16 vt + 15 (vt = wave), all tokens
     const int vt = wave, ct = wave;
@@ -539,10 +549,10 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         const int ix = (16 * rt + r16) * D + 16 * vt + g4;
         const bool ok = !VL || 16 * rt + r16 < len;
         const floatx4 v4 = cvt_raw4<false>(Raw4<false>{vr[rt]});
-        const floatx4 w4 = WS ? splat4(bf16_to_f32((uint16_t)wr[rt].x)) : cvt_raw4<false>(Raw4<false>{wr[rt]});
+        const floatx4 w4 = gate4(WS ? splat4(bf16_to_f32((uint16_t)wr[rt].x)) : cvt_raw4<false>(Raw4<false>{wr[rt]}));
         if (ok) *reinterpret_cast<floatx4*>(dvg + ix) = x * w4 + poison;
         if constexpr (WS) dwp[rt] = hsum4(x * v4);
-        else if (ok) *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 + poison;
+        else if (ok) *reinterpret_cast<floatx4*>(dwg + ix) = x * v4 * (lg ? w4 * (1.f - w4) : splat4(1.f)) + poison;
     }
     if constexpr (WS) {
 #pragma unroll
@@ -568,7 +578,7 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         if constexpr (BS) brw[tt].x = bg[t];
         else brw[tt] = *reinterpret_cast<const uint2*>(bg + ix);
         if (!ok) {
-            lar[tt] = zero4();
+            lar[tt] = splat4(lg ? __builtin_inff() : 0.f);
             qr[tt] = kr[tt] = brw[tt] = make_uint2(0u, 0u);
         }
     }
@@ -679,6 +689,13 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     // element-wise part, lane (r, g): token 16 tt + r, channels 16 ct + 4g .. +3:
     // g - g_C, E, Qs, Kh, Phi, and the channel-row fragments of -E, Qs and Kh (K = tokens)
     floatx4 gm[NB];
+    if (lg) {
+        // decay logits -> log alpha (kept: the chain rule below needs it)
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lar[tt][i] = gate_log_sigmoid(lar[tt][i]);
+    }
     chunk_decay(lar, gm);
     half8 ef[NK2], qf[NK2], kf[NK2];
     floatx4 phi;
@@ -688,7 +705,7 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         for (int tt = 0; tt < NB; ++tt) {
             const floatx4 eg = expv4(gm[tt]);
             const floatx4 q4 = cvt_raw4<false>(Raw4<false>{qr[tt]}), k4 = cvt_raw4<false>(Raw4<false>{kr[tt]});
-            const floatx4 b4 = BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]});
+            const floatx4 b4 = gate4(BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]}));
             const floatx4 E = b4 * k4 * eg, Qs = q4 * eg, Kh = k4 * expv4(-gm[tt]);
             p2 += Qs * A1[tt] - E * A2[tt];
             eT[tt] = swap16(to_h4(-E), id);     // -E: the dA tiles hold -dA
@@ -740,7 +757,7 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         const bool ok = !VL || 16 * tt + r16 < len;
         const floatx4 eg = expv4(gm[tt]), ek = expv4(-gm[tt]);
         const floatx4 q4 = cvt_raw4<false>(Raw4<false>{qr[tt]}), k4 = cvt_raw4<false>(Raw4<false>{kr[tt]});
-        const floatx4 b4 = BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]});
+        const floatx4 b4 = gate4(BS ? splat4(bf16_to_f32((uint16_t)brw[tt].x)) : cvt_raw4<false>(Raw4<false>{brw[tt]}));
         const floatx4 dQs = A1[tt], dE = -A2[tt], dKh = A3[tt];
         if (ok) {
             *reinterpret_cast<floatx4*>(dqg + ix) = dQs * eg + poison;
@@ -748,13 +765,18 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         }
         const floatx4 dbv = dE * k4 * eg;
         if constexpr (BS) dbs[tt] = hsum4(dbv);
-        else if (ok) *reinterpret_cast<floatx4*>(dbg + ix) = dbv + poison;
+        else if (ok) *reinterpret_cast<floatx4*>(dbg + ix) = dbv * (lg ? b4 * (1.f - b4) : splat4(1.f)) + poison;
         const floatx4 dg = dE * (b4 * k4 * eg) + dQs * (q4 * eg) - dKh * (k4 * ek);
         if constexpr (AS) {
             dgs[tt] = hsum4(dg);
         } else {
             // d log alpha = Phi - (exclusive prefix of dg over the tokens)
-            const floatx4 dla = phi - (carry + (scan16(dg) - dg)) + poison;
+            floatx4 dla = phi - (carry + (scan16(dg) - dg)) + poison;
+            if (lg) {
+                // d/da log sigmoid(a) = sigmoid(-a) = 1 - alpha = -expm1(log alpha)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dla[i] *= -expm1f(lar[tt][i]);
+            }
             if (ok) *reinterpret_cast<floatx4*>(dlag + ix) = dla;
             carry += rowsum16(dg);
         }
@@ -791,12 +813,19 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
                 return a;
             };
             const bool ok = !VL || t < len;
+            // logits: the per-token gate's own value for the chain rule (absent
+            // tokens are not stored; their index is clamped into the chunk)
+            auto dsig = [&](const uint16_t* g) __attribute__((always_inline)) {
+                if (!lg) return 1.f;
+                const float x = gate_sigmoid(bf16_to_f32(g[ok ? t : 0]));
+                return x * (1.f - x);
+            };
             if constexpr (WS) {
-                const float v = wsum(0) + poison;
+                const float v = wsum(0) * dsig(wg) + poison;
                 if (ok) dwg[t] = v;
             }
             if constexpr (BS) {
-                const float v = wsum(1) + poison;
+                const float v = wsum(1) * dsig(bg) + poison;
                 if (ok) dbg[t] = v;
             }
             if constexpr (AS) {
@@ -810,7 +839,9 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
                 float ptot = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) ptot += sPhi[w];
-                if (ok) dlag[t] = ptot - (incl - dg) + poison;
+                float f = 1.f;
+                if (lg) f = -expm1f(gate_log_sigmoid(lag[ok ? t : 0]));
+                if (ok) dlag[t] = (ptot - (incl - dg)) * f + poison;
             }
         }
     }

@@ -49,19 +49,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
 
     // 2. token vectors into LDS
+    // (gates given as logits: alpha = sigmoid(logit), b and w through sigmoid)
+    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
     for (int c = tid; c < DK; c += NT) {
         float qv = load_act1<F32>(p.q, nh * DK + c);
         float kv = load_act1<F32>(p.k, nh * DK + c);
         float la = (p.flags & GDR_ALPHA_SCALAR) ? p.la[nh] : p.la[nh * DK + c];
         float bv = (p.flags & GDR_B_SCALAR) ? load_act1<F32>(p.b, nh) : load_act1<F32>(p.b, nh * DK + c);
+        if (lg) bv = gate_sigmoid(bv);
         s_q[c] = qv;
         s_k[c] = kv;
         s_e[c] = bv * kv;
-        s_a[c] = __expf(la);
+        s_a[c] = lg ? gate_sigmoid(la) : __expf(la);
     }
     for (int j = tid; j < DV; j += NT) {
         float vv = load_act1<F32>(p.v, nh * DV + j);
         float wv = (p.flags & GDR_W_SCALAR) ? load_act1<F32>(p.w, nh) : load_act1<F32>(p.w, nh * DV + j);
+        if (lg) wv = gate_sigmoid(wv);
         s_x[j] = wv * vv;
     }
     __syncthreads();

@@ -32,6 +32,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Gates given as logits (GDR_GATE_LOGITS and the token-mixer kernels): sigmoid
+// and log-sigmoid in fp32.  The hardware reciprocal (1 ulp) replaces IEEE
+// division, which costs about ten instructions per value.
+__device__ __forceinline__ float gate_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float gate_sigmoid(float x) { return gate_rcp(1.f + __expf(-x)); }
+// log(1 + e) for e in [0, 1] with relative accuracy for tiny e: with u = 1 + e
+// rounded, log(u) * e / (u - 1) cancels the rounding of u (Goldberg, "What
+// every computer scientist should know about floating-point arithmetic",
+// 1991, Theorem 4); u == 1 means e is below half an ulp of 1, where log1p(e) = e.
+__device__ __forceinline__ float gate_log1p_small(float e) {
+    const float u = 1.f + e;
+    return u == 1.f ? e : __logf(u) * e * gate_rcp(u - 1.f);
+}
+// log(sigmoid(z)) = min(z, 0) - log(1 + exp(-|z|)): no overflow for either sign,
+// the tiny values for large z keep their relative accuracy, and z = +inf gives 0
+__device__ __forceinline__ float gate_log_sigmoid(float z) {
+    return fminf(z, 0.f) - gate_log1p_small(__expf(-fabsf(z)));
+}
+
 // Load 4 consecutive activations starting at element index `idx`.
 template <bool F32>
 __device__ __forceinline__ floatx4 load_act4(const void* base, size_t idx) {

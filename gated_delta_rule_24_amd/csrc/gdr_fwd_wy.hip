@@ -144,6 +144,10 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     // as zeros, log alpha 0 included, so they leave the state unchanged; the
     // loads themselves go to the chunk's first token)
     const u32x4 z4 = {0u, 0u, 0u, 0u};
+    // gates given as logits: absent tokens get the decay logit +inf (log sigmoid = 0)
+    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    const float la_absent = lg ? __builtin_inff() : 0.f;
+    const floatx4 la_absent4 = {la_absent, la_absent, la_absent, la_absent};
     auto issue = [&](size_t tok0, int len, int group) __attribute__((always_inline)) {
         if (group < 2) {
 #pragma unroll
@@ -167,7 +171,7 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                     }
                     if (!ok) {
                         rb[j] = z4;
-                        rla[j][0] = rla[j][1] = zero4();
+                        rla[j][0] = rla[j][1] = la_absent4;
                     }
                 }
             }
@@ -213,6 +217,16 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
         // ---------------- element-wise: in-chunk prefix, E, Qs, Kh, X (fp32 -> f16)
         float gl[TPP][8];
         floatx4 off[2];
+        if (lg) {
+            // decay logits -> log alpha = log sigmoid(logit), fp32
+#pragma unroll
+            for (int j = 0; j < TPP; ++j)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!AS || (hh == 0 && i == 0)) rla[j][hh][i] = gate_log_sigmoid(rla[j][hh][i]);
+        }
         {
             float run[8];
 #pragma unroll
@@ -279,11 +293,16 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 unpack8(rq[j], q8);
                 unpack8(rk[j], k8);
                 if constexpr (BS) {
-                    const float bs = __uint_as_float(rb[j][0] << 16);
+                    float bs = __uint_as_float(rb[j][0] << 16);
+                    if (lg) bs = gate_sigmoid(bs);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) b8[i] = bs;
                 } else {
                     unpack8(rb[j], b8);
+                    if (lg) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) b8[i] = gate_sigmoid(b8[i]);
+                    }
                 }
                 half8 e, qq, kk;
 #pragma unroll
@@ -315,11 +334,16 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
                 float v8[8], w8[8];
                 unpack8(rv[j], v8);
                 if constexpr (WS) {
-                    const float wsv = __uint_as_float(rw[j][0] << 16);
+                    float wsv = __uint_as_float(rw[j][0] << 16);
+                    if (lg) wsv = gate_sigmoid(wsv);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = wsv;
                 } else {
                     unpack8(rw[j], w8);
+                    if (lg) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) w8[i] = gate_sigmoid(w8[i]);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) xt[i][j] = (_Float16)(v8[i] * w8[i]);

@@ -33,23 +33,9 @@ constexpr float kEps = 1e-6f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The outputs are rounded to bf16 (8 significant bits), so the hardware
-// reciprocal (1 ulp in fp32) replaces IEEE division, which costs about ten
-// instructions per value on a path that is otherwise a handful of them.
-__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float sigmoid(float x) { return rcp(1.f + __expf(-x)); }
-__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
-// log(1 + e) for e in [0, 1] with relative accuracy for tiny e: with u = 1 + e
-// rounded, log(u) * e / (u - 1) cancels the rounding of u (Goldberg, "What
-// every computer scientist should know about floating-point arithmetic",
-// 1991, Theorem 4); u == 1 means e is below half an ulp of 1, where log1p(e) = e.
-__device__ __forceinline__ float log1p_small(float e) {
-    const float u = 1.f + e;
-    return u == 1.f ? e : __logf(u) * e * rcp(u - 1.f);
-}
-// log(sigmoid(z)) = min(z, 0) - log(1 + exp(-|z|)): no overflow for either sign,
-// and the tiny values for large z keep their relative accuracy (log alpha stays fp32)
-__device__ __forceinline__ float log_sigmoid(float z) { return fminf(z, 0.f) - log1p_small(__expf(-fabsf(z))); }
+__device__ __forceinline__ float sigmoid(float x) { return gate_sigmoid(x); }
+__device__ __forceinline__ float silu(float x) { return x * gate_sigmoid(x); }
+__device__ __forceinline__ float log_sigmoid(float z) { return gate_log_sigmoid(z); }
 
 __device__ __forceinline__ void unpack8(u32x4 u, float (&f)[8]) {
 #pragma unroll
@@ -260,7 +246,8 @@ bool mixer_supported(int d) { return d == 64 || d == 128; }
 hipError_t launch_mixer_prologue(const MixerParams& p, int dk, int dv, hipStream_t st) {
     const int ntile = (p.T + mixer::TILE - 1) / mixer::TILE;
     if (p.T == 0) return hipSuccess;
-    dim3 grid((unsigned)((size_t)p.BH * ntile), 6), block(mixer::NT);
+    // with GDR_GATE_LOGITS the gates are left to the recurrence: q, k, v only
+    dim3 grid((unsigned)((size_t)p.BH * ntile), (p.flags & GDR_GATE_LOGITS) ? 3 : 6), block(mixer::NT);
     if (dk == 128 && dv == 128) hipLaunchKernelGGL((mixer::prologue_kernel<128, 128>), grid, block, 0, st, p);
     else if (dk == 64 && dv == 64) hipLaunchKernelGGL((mixer::prologue_kernel<64, 64>), grid, block, 0, st, p);
     else if (dk == 128 && dv == 64) hipLaunchKernelGGL((mixer::prologue_kernel<128, 64>), grid, block, 0, st, p);

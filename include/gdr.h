@@ -79,6 +79,13 @@ typedef enum gdr_status {
 #define GDR_FWD_GENERIC   0x20u  /* forward: use the single-role kernel even where the
                                     pipelined one applies (same results up to rounding
                                     order; for testing)                               */
+#define GDR_GATE_LOGITS   0x40u  /* log_alpha, b and w hold logits: the kernels use
+                                    log alpha = log(sigmoid(log_alpha)), b = sigmoid(b),
+                                    w = sigmoid(w) in fp32 (the token mixer's gating,
+                                    fused into the loads), and the backward returns the
+                                    gradients of the logits.  Two-pass forward and
+                                    backward (workspace, bf16, chunk 64) and decode only;
+                                    GDR_ERR_UNSUPPORTED elsewhere.                      */
 
 #define GDR_ABI_VERSION 2
 

@@ -97,7 +97,7 @@ def test_decode_argument_validation():
     assert call(S=None) == 1
     assert call(N=0) == 1
     assert call(o=MIS) == 1
-    assert call(flags=0x40) == 1
+    assert call(flags=0x80) == 1
     assert call(dk=48) == 2
 
 
@@ -230,3 +230,17 @@ def test_mixer_argument_validation():
     assert epi(ptrs=[A, A, None, A]) == 1
     assert epi(flags=0x4) == 1 and epi(H=0) == 1
     assert epi(dv=16) == 2
+
+
+def test_gate_logits_need_the_two_pass_kernels():
+    """GDR_GATE_LOGITS is taken by the two-pass forward and backward (with a
+    workspace) and by decode; elsewhere the call is refused as unsupported."""
+    lib = _lib()
+    assert _fwd(lib, flags=0x40) == 2                          # no workspace: fused path
+    assert _fwd(lib, flags=0x40 | 0x1) == 2                    # fp32 activations
+    assert _fwd(lib, flags=0x40 | 0x20, ws=A, nbytes=1 << 30) == 2   # forced generic kernel
+    nb = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 32, 0x40)
+    assert nb > 0
+    st = lib.gdr_chunk_bwd(A, A, A, A, A, A, None, A, None, A, A, A, A, A, A, None, 1, 1, 64, 128, 128,
+                           32, 0x40, A, nb, None)
+    assert st == 2                                            # chunks of 32: no two-pass backward
