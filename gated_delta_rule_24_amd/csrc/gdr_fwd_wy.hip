@@ -85,7 +85,7 @@ __device__ __forceinline__ void chunk_item(const FwdParams& p, int CN, int idx, 
     }
 }
 
-template <int DK, int DV, bool AS, bool BS, bool WS, bool BL, bool VL>
+template <int DK, int DV, bool AS, bool BS, bool WS, bool BL, bool VL, bool LG>
 __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdParams p, unsigned char* ws) {
     using L = PrepLayout<DK, DV>;
     constexpr int NT = L::NT, NW = NT / 64;
@@ -144,8 +144,9 @@ __global__ __launch_bounds__((PrepLayout<DK, DV>::NT), 1) void wy_kernel(FwdPara
     // as zeros, log alpha 0 included, so they leave the state unchanged; the
     // loads themselves go to the chunk's first token)
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    // gates given as logits: absent tokens get the decay logit +inf (log sigmoid = 0)
-    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    // gates given as logits (LG, GDR_GATE_LOGITS): absent tokens get the decay
+    // logit +inf (log sigmoid = 0)
+    constexpr bool lg = LG;
     const float la_absent = lg ? __builtin_inff() : 0.f;
     const floatx4 la_absent4 = {la_absent, la_absent, la_absent, la_absent};
     auto issue = [&](size_t tok0, int len, int group) __attribute__((always_inline)) {
@@ -952,15 +953,16 @@ constexpr int kChainStrips = 1;
 template <int DK, int DV, bool AS, bool BS, bool WS, bool BL, bool VL>
 static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int passes) {
     using LP = PrepLayout<DK, DV>;
-    auto kp = wy_kernel<DK, DV, AS, BS, WS, BL, VL>;
+    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    auto kp = lg ? wy_kernel<DK, DV, AS, BS, WS, BL, VL, true> : wy_kernel<DK, DV, AS, BS, WS, BL, VL, false>;
     auto ks = chain_kernel<DK, DV, kChainStrips, VL>;
     constexpr size_t RB = BL ? Rec<DK, DV>::bwd_bytes : Rec<DK, DV>::bytes;
-    static bool attr_done = false;
-    if (!attr_done) {
+    static bool attr_done[2] = {false, false};
+    if (!attr_done[lg]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::bytes);
         if (e != hipSuccess) return e;
-        attr_done = true;
+        attr_done[lg] = true;
     }
     // (packed sequences: the chunk count is on the device; the WY grid is one
     // workgroup per compute unit)
