@@ -358,7 +358,7 @@ __device__ __forceinline__ void chunk_decay(const floatx4 (&la)[4], floatx4 (&gm
     for (int tt = 0; tt < 4; ++tt) gm[tt] -= carry;
 }
 
-template <int D, bool AS, bool BS, bool WS, bool VL>
+template <int D, bool AS, bool BS, bool WS, bool VL, bool LG>
 __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsigned char* ws) {
     using R = Rec<D, D>;
     using SFB = StateFrag<D, D>;
@@ -426,9 +426,10 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         return *reinterpret_cast<const half8*>(base + off + lo16);
     };
     const float poison = *reinterpret_cast<const int*>(rec + R::G + D * 4) ? __builtin_nanf("") : 0.f;
-    // gates given as logits: the values are sigmoid / log sigmoid of the inputs,
-    // the gate gradients are those of the logits (absent tokens: decay logit +inf)
-    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    // gates given as logits (LG, GDR_GATE_LOGITS): the values are sigmoid / log
+    // sigmoid of the inputs, the gate gradients are those of the logits (absent
+    // tokens: decay logit +inf)
+    constexpr bool lg = LG;
     auto gate4 = [&](floatx4 x) __attribute__((always_inline)) {
         if (lg) {
 #pragma unroll
@@ -847,9 +848,9 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
     }
 }
 
-template <int D, bool AS, bool BS, bool WS, bool VL>
+template <int D, bool AS, bool BS, bool WS, bool VL, bool LG>
 static hipError_t launch_wgrad_v(const BwdParams& p, const void* ws, hipStream_t st) {
-    auto k = wgrad_kernel<D, AS, BS, WS, VL>;
+    auto k = wgrad_kernel<D, AS, BS, WS, VL, LG>;
     static bool attr_done = false;
     if (!attr_done) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -866,9 +867,16 @@ static hipError_t launch_wgrad_v(const BwdParams& p, const void* ws, hipStream_t
     return hipGetLastError();
 }
 
+template <int D, bool AS, bool BS, bool WS, bool LG>
+static hipError_t launch_wgrad_l(const BwdParams& p, const void* ws, hipStream_t st) {
+    return p.cu_seqlens ? launch_wgrad_v<D, AS, BS, WS, true, LG>(p, ws, st)
+                        : launch_wgrad_v<D, AS, BS, WS, false, LG>(p, ws, st);
+}
+
 template <int D, bool AS, bool BS, bool WS>
 static hipError_t launch_wgrad_t(const BwdParams& p, const void* ws, hipStream_t st) {
-    return p.cu_seqlens ? launch_wgrad_v<D, AS, BS, WS, true>(p, ws, st) : launch_wgrad_v<D, AS, BS, WS, false>(p, ws, st);
+    return (p.flags & GDR_GATE_LOGITS) ? launch_wgrad_l<D, AS, BS, WS, true>(p, ws, st)
+                                       : launch_wgrad_l<D, AS, BS, WS, false>(p, ws, st);
 }
 
 template <int D>
