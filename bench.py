@@ -67,6 +67,11 @@ MIX_EPI_BYTES_PER_TOKEN = FD * 4 + FD * 2 + FD * 2
 # with the gating fused into the recurrence's loads (GDR_GATE_LOGITS) the
 # prologue reads and writes q, k, v only
 MIX_QKV_BYTES_PER_TOKEN = 2 * 3 * FD * 2
+# backward: the prologue's q, k, v paths read the projection outputs (bf16) and
+# the gradients of q, k, v (fp32) and write the projections' gradients (fp32);
+# the epilogue reads o, dy (fp32) and the gate (bf16), writes d_o and dg (fp32)
+MIX_PRO_BWD_BYTES_PER_TOKEN = 3 * (FD * 2 + FD * 4 + FD * 4)
+MIX_EPI_BWD_BYTES_PER_TOKEN = FD * 4 + FD * 4 + FD * 2 + 2 * FD * 4
 
 # backward workload: B=1, H=32, T=16384, d=128, chunk 64; algorithmic bytes per
 # head-token: inputs q, k, b, v, w, dO bf16 + log-decay fp32, gradients dq, dk,
@@ -309,11 +314,31 @@ def bench_mixer(steps, warmup):
     def fwd_logits():
         gdr.gdr_chunk_fwd(out["q"], out["k"], out["v"], d["a_pre"], d["b_pre"], d["w_pre"], S0, of, None,
                           FB, FH, FT, FD, FD, FC, fl, ws, nb)
+    # backward of the prologue's q, k, v paths and of the epilogue
+    gq = torch.randn((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
+    gb = {n: torch.empty((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
+          for n in ("dq_pre", "dk_pre", "dv_pre", "d_o", "dg")}
+    gt = {n: torch.empty_like(d[n]) for n in ("conv_q", "conv_k", "conv_v")}
+    dwn = torch.empty((FD,), dtype=torch.float32, device="cuda")
+    nbw = gdr.gdr_mixer_bwd_workspace_bytes(FB, FH, FT, FD, FD)
+    wsb = torch.empty(nbw, dtype=torch.uint8, device="cuda")
+
+    def pro_bwd():
+        gdr.gdr_mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                                   d["conv_v"], gq, gq, gq, gb["dq_pre"], gb["dk_pre"], gb["dv_pre"],
+                                   gt["conv_q"], gt["conv_k"], gt["conv_v"], FB, FH, FT, FD, FD, 0,
+                                   wsb, nbw)
+
+    def epi_bwd():
+        gdr.gdr_mixer_epilogue_bwd(o, d["g"], d["norm_weight"], gq, gb["d_o"], gb["dg"], dwn, FB, FH,
+                                   FT, FD, 0, wsb, nbw)
     _, pro_ms = time_loop(pro, steps, warmup)
     _, epi_ms = time_loop(epi, steps, warmup)
     _, qkv_ms = time_loop(qkv, steps, warmup)
     _, fl_ms = time_loop(fwd_logits, steps, warmup)
-    return pro_ms, epi_ms, qkv_ms, fl_ms
+    _, pb_ms = time_loop(pro_bwd, steps, warmup)
+    _, eb_ms = time_loop(epi_bwd, steps, warmup)
+    return pro_ms, epi_ms, qkv_ms, fl_ms, pb_ms, eb_ms
 
 
 def bench_copy(steps, warmup):
@@ -409,9 +434,10 @@ def main():
         log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
         return
     if args.only == "mixer":
-        pm, em, qm, fm = bench_mixer(args.steps, args.warmup)
+        pm, em, qm, fm, pbm, ebm = bench_mixer(args.steps, args.warmup)
         log(f"mixer prologue {pm * 1e3:.1f} us, epilogue {em * 1e3:.1f} us, q/k/v-only prologue "
-            f"{qm * 1e3:.1f} us, forward on gate logits {fm * 1e3:.1f} us")
+            f"{qm * 1e3:.1f} us, forward on gate logits {fm * 1e3:.1f} us, prologue backward "
+            f"{pbm * 1e3:.1f} us, epilogue backward {ebm * 1e3:.1f} us")
         return
     if args.only == "bwd_varlen":
         lengths, w, e = bench_bwd_varlen(args.steps, args.warmup)
@@ -446,7 +472,7 @@ def main():
     log(f"varlen fwd ({len(lengths)} sequences, longest {max(lengths)}): "
         f"{var_ev * 1e3:.1f} us/step, {var_gbs:.0f} GB/s")
 
-    mix_pro_ms, mix_epi_ms, mix_qkv_ms, mix_fl_ms = bench_mixer(args.steps, args.warmup)
+    mix_pro_ms, mix_epi_ms, mix_qkv_ms, mix_fl_ms, mix_pb_ms, mix_eb_ms = bench_mixer(args.steps, args.warmup)
     ntok_mix = FB * FH * FT
     mix_pro_gbs = ntok_mix * MIX_PRO_BYTES_PER_TOKEN / (mix_pro_ms * 1e-3) / 1e9
     mix_epi_gbs = ntok_mix * MIX_EPI_BYTES_PER_TOKEN / (mix_epi_ms * 1e-3) / 1e9
@@ -541,6 +567,14 @@ def main():
                 "fwd_on_logits_us": mix_fl_ms * 1e3,
                 "block_us": (mix_qkv_ms + mix_fl_ms + mix_epi_ms) * 1e3,
                 "block_us_unfused": (mix_pro_ms + ev_ms + mix_epi_ms) * 1e3,
+            },
+            "backward": {
+                "prologue_qkv_bwd_us": mix_pb_ms * 1e3,
+                "prologue_qkv_bwd_GB_per_s":
+                    ntok_mix * MIX_PRO_BWD_BYTES_PER_TOKEN / (mix_pb_ms * 1e-3) / 1e9,
+                "epilogue_bwd_us": mix_eb_ms * 1e3,
+                "epilogue_bwd_GB_per_s":
+                    ntok_mix * MIX_EPI_BWD_BYTES_PER_TOKEN / (mix_eb_ms * 1e-3) / 1e9,
             },
         },
         "backward": {

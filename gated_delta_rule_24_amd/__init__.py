@@ -84,6 +84,12 @@ def _load():
         lib.gdr_mixer_prologue.restype = I
         lib.gdr_mixer_epilogue.argtypes = [P] * 4 + [I] * 4 + [U, P]
         lib.gdr_mixer_epilogue.restype = I
+        lib.gdr_mixer_bwd_workspace_bytes.argtypes = [I] * 5
+        lib.gdr_mixer_bwd_workspace_bytes.restype = S
+        lib.gdr_mixer_prologue_bwd.argtypes = [P] * 15 + [I] * 5 + [U, P, S, P]
+        lib.gdr_mixer_prologue_bwd.restype = I
+        lib.gdr_mixer_epilogue_bwd.argtypes = [P] * 7 + [I] * 4 + [U, P, S, P]
+        lib.gdr_mixer_epilogue_bwd.restype = I
         _lib = lib
     return _lib
 
@@ -97,7 +103,8 @@ EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_works
                     "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
                     "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
                     "gdr_chunk_bwd_varlen_workspace_bytes", "gdr_chunk_bwd_varlen",
-                    "gdr_mixer_prologue", "gdr_mixer_epilogue")
+                    "gdr_mixer_prologue", "gdr_mixer_epilogue", "gdr_mixer_bwd_workspace_bytes",
+                    "gdr_mixer_prologue_bwd", "gdr_mixer_epilogue_bwd")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -220,6 +227,29 @@ def gdr_mixer_epilogue(o, g, norm_weight, y, B, H, T, d_v, flags=0, stream=None)
     st = _load().gdr_mixer_epilogue(_ptr(o), _ptr(g), _ptr(norm_weight), _ptr(y), B, H, T, d_v,
                                     flags, _stream(stream))
     _check("gdr_mixer_epilogue", st)
+
+
+def gdr_mixer_bwd_workspace_bytes(B, H, T, d_k, d_v) -> int:
+    return int(_load().gdr_mixer_bwd_workspace_bytes(B, H, T, d_k, d_v))
+
+
+def gdr_mixer_prologue_bwd(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, dq, dk, dv, dq_pre, dk_pre,
+                           dv_pre, dconv_q, dconv_k, dconv_v, B, H, T, d_k, d_v, flags, workspace,
+                           workspace_bytes, stream=None):
+    st = _load().gdr_mixer_prologue_bwd(*[_ptr(x) for x in (q_pre, k_pre, v_pre, conv_q, conv_k,
+                                                            conv_v, dq, dk, dv, dq_pre, dk_pre,
+                                                            dv_pre, dconv_q, dconv_k, dconv_v)],
+                                        B, H, T, d_k, d_v, flags, _ptr(workspace), workspace_bytes,
+                                        _stream(stream))
+    _check("gdr_mixer_prologue_bwd", st)
+
+
+def gdr_mixer_epilogue_bwd(o, g, norm_weight, dy, d_o, dg, dnorm_weight, B, H, T, d_v, flags,
+                           workspace, workspace_bytes, stream=None):
+    st = _load().gdr_mixer_epilogue_bwd(_ptr(o), _ptr(g), _ptr(norm_weight), _ptr(dy), _ptr(d_o),
+                                        _ptr(dg), _ptr(dnorm_weight), B, H, T, d_v, flags,
+                                        _ptr(workspace), workspace_bytes, _stream(stream))
+    _check("gdr_mixer_epilogue_bwd", st)
 
 
 # ---------------------------------------------------------------------------
@@ -385,3 +415,40 @@ def mixer_epilogue(o, g, norm_weight, stream=None):
     y = torch.empty(o.shape, dtype=torch.bfloat16, device=o.device)
     gdr_mixer_epilogue(o, g, norm_weight, y, B, H, T, dv, 0, stream)
     return y
+
+
+def mixer_prologue_bwd(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, dq, dk, dv, stream=None):
+    """Gradients of the prologue's q, k, v paths: dict dq_pre, dk_pre, dv_pre
+    (fp32 [B,H,T,d]) and dconv_q, dconv_k, dconv_v (fp32 [H,d,4])."""
+    B, H, T, dk_ = q_pre.shape
+    dv_ = v_pre.shape[-1]
+    f32 = torch.float32
+    out = dict(dq_pre=torch.empty(q_pre.shape, dtype=f32, device=q_pre.device),
+               dk_pre=torch.empty(k_pre.shape, dtype=f32, device=q_pre.device),
+               dv_pre=torch.empty(v_pre.shape, dtype=f32, device=q_pre.device),
+               dconv_q=torch.empty_like(conv_q), dconv_k=torch.empty_like(conv_k),
+               dconv_v=torch.empty_like(conv_v))
+    nb = gdr_mixer_bwd_workspace_bytes(B, H, T, dk_, dv_)
+    if nb == 0:
+        raise GdrError("gdr_mixer_bwd_workspace_bytes", 2)
+    ws = torch.empty(nb, dtype=torch.uint8, device=q_pre.device)
+    gdr_mixer_prologue_bwd(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, dq, dk, dv, out["dq_pre"],
+                           out["dk_pre"], out["dv_pre"], out["dconv_q"], out["dconv_k"],
+                           out["dconv_v"], B, H, T, dk_, dv_, 0, ws, nb, stream)
+    return out
+
+
+def mixer_epilogue_bwd(o, g, norm_weight, dy, stream=None):
+    """Gradients of the epilogue: dict d_o, dg (fp32 [B,H,T,dv]), dnorm_weight (fp32 [dv])."""
+    B, H, T, dv_ = o.shape
+    f32 = torch.float32
+    out = dict(d_o=torch.empty(o.shape, dtype=f32, device=o.device),
+               dg=torch.empty(o.shape, dtype=f32, device=o.device),
+               dnorm_weight=torch.empty((dv_,), dtype=f32, device=o.device))
+    nb = gdr_mixer_bwd_workspace_bytes(B, H, T, dv_, dv_)
+    if nb == 0:
+        raise GdrError("gdr_mixer_bwd_workspace_bytes", 2)
+    ws = torch.empty(nb, dtype=torch.uint8, device=o.device)
+    gdr_mixer_epilogue_bwd(o, g, norm_weight, dy, out["d_o"], out["dg"], out["dnorm_weight"], B, H, T,
+                           dv_, 0, ws, nb, stream)
+    return out

@@ -303,4 +303,63 @@ gdr_status gdr_mixer_epilogue(const float* o, const void* g, const float* norm_w
     return from_hip(gdr::launch_mixer_epilogue(p, d_v, (hipStream_t)stream));
 }
 
+size_t gdr_mixer_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v) {
+    if (B < 1 || H < 1 || T < 1 || d_k != d_v || !gdr::mixer_supported(d_k)) return 0;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * ((T + 63) / 64) > (1LL << 31) - 1) return 0;
+    const size_t pro = gdr::mixer_prologue_bwd_workspace_bytes(B * H, T, d_k, d_v);
+    const size_t epi = gdr::mixer_epilogue_bwd_workspace_bytes(d_v);
+    return pro > epi ? pro : epi;
+}
+
+gdr_status gdr_mixer_prologue_bwd(const void* q_pre, const void* k_pre, const void* v_pre,
+                                  const float* conv_q, const float* conv_k, const float* conv_v,
+                                  const float* dq, const float* dk, const float* dv, float* dq_pre,
+                                  float* dk_pre, float* dv_pre, float* dconv_q, float* dconv_k,
+                                  float* dconv_v, int B, int H, int T, int d_k, int d_v,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (flags != 0) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 1) return GDR_ERR_INVALID_ARG;
+    if (d_k != d_v || !gdr::mixer_supported(d_k)) return GDR_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, dq, dk, dv, dq_pre, dk_pre,
+                          dv_pre, dconv_q, dconv_k, dconv_v, workspace};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    const size_t need = gdr_mixer_bwd_workspace_bytes(B, H, T, d_k, d_v);
+    if (need == 0) return GDR_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+    gdr::MixerBwdParams p;
+    p.q_pre = q_pre; p.k_pre = k_pre; p.v_pre = v_pre;
+    p.conv_q = conv_q; p.conv_k = conv_k; p.conv_v = conv_v;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dq_pre = dq_pre; p.dk_pre = dk_pre; p.dv_pre = dv_pre;
+    p.dconv_q = dconv_q; p.dconv_k = dconv_k; p.dconv_v = dconv_v;
+    p.part = reinterpret_cast<float*>(workspace);
+    p.BH = B * H; p.H = H; p.T = T;
+    return from_hip(gdr::launch_mixer_prologue_bwd(p, d_k, d_v, (hipStream_t)stream));
+}
+
+gdr_status gdr_mixer_epilogue_bwd(const float* o, const void* g, const float* norm_weight,
+                                  const float* dy, float* d_o, float* dg, float* dnorm_weight,
+                                  int B, int H, int T, int d_v, uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (flags != 0) return GDR_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 1) return GDR_ERR_INVALID_ARG;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * T > (1LL << 40)) return GDR_ERR_INVALID_ARG;
+    if (!gdr::mixer_supported(d_v)) return GDR_ERR_UNSUPPORTED;
+    const void* ptrs[] = {o, g, norm_weight, dy, d_o, dg, dnorm_weight, workspace};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    if (workspace_bytes < gdr::mixer_epilogue_bwd_workspace_bytes(d_v)) return GDR_ERR_WORKSPACE;
+    gdr_status ds = check_device();
+    if (ds != GDR_OK) return ds;
+    gdr::EpilogueBwdParams p;
+    p.o = o; p.g = g; p.norm_weight = norm_weight; p.dy = dy;
+    p.d_o = d_o; p.dg = dg; p.dnorm_weight = dnorm_weight;
+    p.part = reinterpret_cast<float*>(workspace);
+    p.rows = (long long)B * H * T;
+    return from_hip(gdr::launch_mixer_epilogue_bwd(p, d_v, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -163,7 +163,44 @@ struct EpilogueParams {
     void* y;               // [rows, DV] bf16
     long long rows;        // B * H * T
 };
+struct MixerBwdParams {
+    const void* q_pre;     // forward inputs, as MixerParams
+    const void* k_pre;
+    const void* v_pre;
+    const float* conv_q;
+    const float* conv_k;
+    const float* conv_v;
+    const float* dq;       // gradients of the prologue's q, k, v outputs, fp32
+    const float* dk;
+    const float* dv;
+    float* dq_pre;         // outputs, fp32, shaped as the inputs
+    float* dk_pre;
+    float* dv_pre;
+    float* dconv_q;        // fp32 [H, d, kConvTaps], written
+    float* dconv_k;
+    float* dconv_v;
+    float* part;           // workspace: per-tile tap-gradient partials
+    int BH;
+    int H;
+    int T;
+};
+struct EpilogueBwdParams {
+    const float* o;
+    const void* g;
+    const float* norm_weight;
+    const float* dy;       // gradient of y, fp32
+    float* d_o;            // outputs, fp32
+    float* dg;
+    float* dnorm_weight;   // [DV], written
+    float* part;           // workspace: per-workgroup norm-weight partials
+    long long rows;
+};
+constexpr int kEpilogueBwdBlocks = 1024;   // workgroups of the epilogue backward
 bool mixer_supported(int d);
+size_t mixer_prologue_bwd_workspace_bytes(int BH, int T, int dk, int dv);
+size_t mixer_epilogue_bwd_workspace_bytes(int dv);
+hipError_t launch_mixer_prologue_bwd(const MixerBwdParams& p, int dk, int dv, hipStream_t st);
+hipError_t launch_mixer_epilogue_bwd(const EpilogueBwdParams& p, int dv, hipStream_t st);
 hipError_t launch_mixer_prologue(const MixerParams& p, int dk, int dv, hipStream_t st);
 hipError_t launch_mixer_epilogue(const EpilogueParams& p, int dv, hipStream_t st);
 

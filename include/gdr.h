@@ -309,6 +309,41 @@ gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* 
 gdr_status gdr_mixer_epilogue(const float* o, const void* g, const float* norm_weight, void* y,
                               int B, int H, int T, int d_v, uint32_t flags, void* stream);
 
+/*
+ * Backward of the token-mixer prologue's q, k and v paths and of the
+ * epilogue, for training through the block.  (With GDR_GATE_LOGITS the
+ * recurrence's backward already returns the gate logits' gradients, so the
+ * gate paths need nothing here.)
+ *
+ * gdr_mixer_prologue_bwd: given dq, dk, dv (fp32 [B, H, T, d], the gradients
+ * of the prologue's outputs, e.g. from gdr_chunk_bwd), writes the gradients
+ * of the projection outputs dq_pre, dk_pre, dv_pre (fp32, shaped as q_pre,
+ * k_pre, v_pre) and of the convolution taps dconv_q, dconv_k, dconv_v (fp32
+ * [H, d, 4], summed over the batch and the tokens in a fixed order, so the
+ * result is deterministic).  The forward's values are recomputed from q_pre,
+ * k_pre, v_pre and the taps.
+ * gdr_mixer_epilogue_bwd: given dy (fp32 [B, H, T, d_v]), writes d_o and dg
+ * (fp32 [B, H, T, d_v]) and dnorm_weight (fp32 [d_v], summed over all rows
+ * in a fixed order).
+ * Both need a workspace of gdr_mixer_bwd_workspace_bytes() bytes (one buffer
+ * serves both calls on one stream); outputs must not alias inputs; flags
+ * must be 0.  Supported: d_k = d_v in {64, 128}, T >= 1.
+ */
+size_t gdr_mixer_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v);
+
+gdr_status gdr_mixer_prologue_bwd(const void* q_pre, const void* k_pre, const void* v_pre,
+                                  const float* conv_q, const float* conv_k, const float* conv_v,
+                                  const float* dq, const float* dk, const float* dv,
+                                  float* dq_pre, float* dk_pre, float* dv_pre,
+                                  float* dconv_q, float* dconv_k, float* dconv_v,
+                                  int B, int H, int T, int d_k, int d_v, uint32_t flags,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+gdr_status gdr_mixer_epilogue_bwd(const float* o, const void* g, const float* norm_weight,
+                                  const float* dy, float* d_o, float* dg, float* dnorm_weight,
+                                  int B, int H, int T, int d_v, uint32_t flags,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

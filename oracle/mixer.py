@@ -1,4 +1,4 @@
-"""Oracle for the token-mixer prologue and epilogue: plain fp64 numpy.
+"""Oracle for the token-mixer prologue and epilogue: plain fp64 on the CPU.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite and bench.py's CPU-baseline
 leg may import this module.  The HIP library never calls it, and the two
@@ -22,70 +22,102 @@ taken is:
   the heads;
 - the decay gate is a sigmoid like the others (the Q&A page writes alpha as
   a sigmoid of a projection), so log alpha = log(sigmoid(a_pre)).
-Every function works in float64 on whatever array it is given.
+
+The definitions are written once, as plain float64 torch operations on the
+CPU (numpy arrays in and out).  The backward functions differentiate exactly
+these definitions with torch.autograd (reverse mode as a library step); the
+tests pin them with central finite differences of the forward.
 """
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 TAPS = 4
 EPS = 1e-6
 
 
-def _f64(x):
-    return np.asarray(x, dtype=np.float64)
+def _t(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float64))
 
 
-def causal_conv(x, taps):
-    """y[..., h, t, c] = sum_j taps[h, c, j] * x[..., h, t - j, c], over j with t - j >= 0.
+# ------------------------------------------------------------ definitions (torch fp64)
 
-    x: [..., H, T, D]; taps: [H, D, TAPS]."""
-    x = _f64(x)
-    taps = _f64(taps)
+def _causal_conv(x, taps):
+    """y[..., h, t, c] = sum_j taps[h, c, j] * x[..., h, t - j, c], over j with t - j >= 0."""
     T = x.shape[-2]
-    y = np.zeros_like(x)
-    for j in range(taps.shape[-1]):
-        if j >= T:
-            break
+    y = torch.zeros_like(x)
+    for j in range(min(taps.shape[-1], T)):
         # token t takes x[t - j]: shift the sequence down by j, zeros in front
-        shifted = np.zeros_like(x)
+        shifted = torch.zeros_like(x)
         shifted[..., j:, :] = x[..., :T - j, :]
-        y += shifted * taps[:, None, :, j]
+        y = y + shifted * taps[:, None, :, j]
     return y
 
 
+def _silu(x):
+    return x / (1.0 + torch.exp(-x))
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + torch.exp(-x))
+
+
+def _log_sigmoid(x):
+    # -log(1 + exp(-x)), in a form that overflows for neither sign
+    return -torch.logaddexp(torch.zeros_like(x), -x)
+
+
+def _l2norm(x):
+    return x / torch.sqrt(torch.sum(x * x, dim=-1, keepdim=True) + EPS)
+
+
+def _rms_norm(x, weight):
+    return x / torch.sqrt(torch.mean(x * x, dim=-1, keepdim=True) + EPS) * weight
+
+
+def _stream(x, taps, l2):
+    y = _silu(_causal_conv(x, taps))
+    return _l2norm(y) if l2 else y
+
+
+def _epilogue(o, g, weight):
+    return _rms_norm(o, weight) * _silu(g)
+
+
+# ------------------------------------------------------------ numpy-facing forward
+
+def causal_conv(x, taps):
+    """x: [..., H, T, D]; taps: [H, D, TAPS]."""
+    return _causal_conv(_t(x), _t(taps)).numpy()
+
+
 def silu(x):
-    x = _f64(x)
-    return x / (1.0 + np.exp(-x))
+    return _silu(_t(x)).numpy()
 
 
 def sigmoid(x):
-    x = _f64(x)
-    return 1.0 / (1.0 + np.exp(-x))
+    return _sigmoid(_t(x)).numpy()
 
 
 def log_sigmoid(x):
-    """log(1 / (1 + exp(-x))) = -log(1 + exp(-x)), written with logaddexp so
-    that neither sign overflows."""
-    return -np.logaddexp(0.0, -_f64(x))
+    return _log_sigmoid(_t(x)).numpy()
 
 
 def l2norm(x):
-    x = _f64(x)
-    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + EPS)
+    return _l2norm(_t(x)).numpy()
 
 
 def rms_norm(x, weight):
-    x = _f64(x)
-    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + EPS) * _f64(weight)
+    return _rms_norm(_t(x), _t(weight)).numpy()
 
 
 def prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre):
     """The recurrence's inputs from the projection outputs ([B, H, T, d]
     streams; gate logits [B, H, T, d] or [B, H, T])."""
-    return dict(q=l2norm(silu(causal_conv(q_pre, conv_q))),
-                k=l2norm(silu(causal_conv(k_pre, conv_k))),
-                v=silu(causal_conv(v_pre, conv_v)),
+    return dict(q=_stream(_t(q_pre), _t(conv_q), True).numpy(),
+                k=_stream(_t(k_pre), _t(conv_k), True).numpy(),
+                v=_stream(_t(v_pre), _t(conv_v), False).numpy(),
                 log_alpha=log_sigmoid(a_pre),
                 b=sigmoid(b_pre),
                 w=sigmoid(w_pre))
@@ -93,4 +125,24 @@ def prologue(q_pre, k_pre, v_pre, conv_q, conv_k, conv_v, a_pre, b_pre, w_pre):
 
 def epilogue(o, g, norm_weight):
     """RMS-normalised output times the SiLU output gate ([B, H, T, d_v])."""
-    return rms_norm(o, norm_weight) * silu(g)
+    return _epilogue(_t(o), _t(g), _t(norm_weight)).numpy()
+
+
+# ------------------------------------------------------------ reverse mode
+
+def _grad(f, inputs, cotangent):
+    xs = [_t(x).requires_grad_(True) for x in inputs]
+    y = f(*xs)
+    (y * _t(cotangent)).sum().backward()
+    return [x.grad.numpy() for x in xs]
+
+
+def stream_bwd(x_pre, taps, dy, l2):
+    """Gradients of <dy, stream(x_pre, taps)> (the q / k path with l2=True,
+    the v path with l2=False) w.r.t. x_pre and the taps."""
+    return tuple(_grad(lambda x, w: _stream(x, w, l2), (x_pre, taps), dy))
+
+
+def epilogue_bwd(o, g, norm_weight, dy):
+    """Gradients of <dy, epilogue(o, g, w)> w.r.t. o, g and w."""
+    return tuple(_grad(_epilogue, (o, g, norm_weight), dy))

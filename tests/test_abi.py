@@ -244,3 +244,22 @@ def test_gate_logits_need_the_two_pass_kernels():
     st = lib.gdr_chunk_bwd(A, A, A, A, A, A, None, A, None, A, A, A, A, A, A, None, 1, 1, 64, 128, 128,
                            32, 0x40, A, nb, None)
     assert st == 2                                            # chunks of 32: no two-pass backward
+
+
+def test_mixer_backward_validation():
+    lib = _lib()
+    nb = lib.gdr_mixer_bwd_workspace_bytes(2, 3, 200, 128, 128)
+    # the larger of: three blocks of per-tile tap partials ((B*H) x ceil(T/64) tiles x
+    # d x 4 taps, fp32) and the epilogue's 1024 per-workgroup rows of d partials
+    assert nb == max(3 * 6 * 4 * 128 * 4 * 4, 1024 * 128 * 4)
+    assert lib.gdr_mixer_bwd_workspace_bytes(4, 16, 4096, 128, 128) == 3 * 64 * 64 * 128 * 4 * 4
+    assert lib.gdr_mixer_bwd_workspace_bytes(1, 1, 8, 64, 64) == 1024 * 64 * 4   # epilogue partials
+    assert lib.gdr_mixer_bwd_workspace_bytes(1, 1, 64, 128, 64) == 0
+    assert lib.gdr_mixer_bwd_workspace_bytes(1, 1, 0, 128, 128) == 0
+    args = [A] * 15
+    assert lib.gdr_mixer_prologue_bwd(*args, 2, 3, 200, 128, 128, 0, A, nb - 1, None) == 3
+    assert lib.gdr_mixer_prologue_bwd(*args, 2, 3, 200, 128, 128, 1, A, nb, None) == 1
+    assert lib.gdr_mixer_prologue_bwd(*args, 2, 3, 200, 128, 64, 0, A, nb, None) == 2
+    assert lib.gdr_mixer_prologue_bwd(*([A] * 14 + [None]), 2, 3, 200, 128, 128, 0, A, nb, None) == 1
+    assert lib.gdr_mixer_epilogue_bwd(*([A] * 7), 1, 1, 8, 64, 0, A, 1024 * 64 * 4 - 1, None) == 3
+    assert lib.gdr_mixer_epilogue_bwd(*([A] * 7), 1, 1, 8, 96, 0, A, 1 << 20, None) == 2

@@ -141,3 +141,126 @@ def test_prologue_workload_shape_sampled_heads():
                              sel["conv_v"], sel["a_pre"], sel["b_pre"], sel["w_pre"])
         for n in ("q", "k", "v", "b", "w"):
             _close_bf16(f"{n}[{b},{h}]", got[n][b:b + 1, h:h + 1].float().cpu().numpy(), ref[n])
+
+
+BWD_TOL = 1e-4     # fp32 gradients of exact (bf16-valued) inputs
+
+
+@pytest.mark.parametrize("D,T", [(128, 200), (64, 77), (128, 64), (64, 1)])
+def test_prologue_backward_matches_oracle(D, T):
+    """dq_pre, dk_pre, dv_pre and the tap gradients against reverse mode of the
+    oracle's q / k path (conv, SiLU, L2 norm) and v path (conv, SiLU)."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    B, H = 2, 3
+    print(f"mixer prologue bwd B={B} H={H} T={T} d={D}", flush=True)
+    m = gs.mixer_inputs(B, H, T, D, D, seed=10)
+    r = np.random.default_rng(11)
+    dy = {n: r.standard_normal((B, H, T, D)).astype(np.float32) for n in ("q", "k", "v")}
+    d = _dev(m)
+    g = gdr.mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], *[torch.from_numpy(dy[n]).cuda() for n in ("q", "k", "v")])
+    torch.cuda.synchronize()
+    for n, l2 in (("q", True), ("k", True), ("v", False)):
+        gx, gw = mixer.stream_bwd(m[f"{n}_pre"], m[f"conv_{n}"], dy[n], l2)
+        ex = rel_err(g[f"d{n}_pre"].cpu().numpy(), gx)
+        ew = rel_err(g[f"dconv_{n}"].cpu().numpy(), gw)
+        print(f"  {n}: d_pre {ex:.2e} dconv {ew:.2e} (tol {BWD_TOL})", flush=True)
+        assert ex <= BWD_TOL and ew <= BWD_TOL, (n, ex, ew)
+
+
+@pytest.mark.parametrize("D,T", [(128, 200), (64, 33)])
+def test_epilogue_backward_matches_oracle(D, T):
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    B, H = 2, 3
+    print(f"mixer epilogue bwd B={B} H={H} T={T} d={D}", flush=True)
+    m = gs.mixer_inputs(B, H, T, 64, D, seed=12)
+    r = np.random.default_rng(13)
+    o = r.standard_normal((B, H, T, D)).astype(np.float32)
+    dy = r.standard_normal((B, H, T, D)).astype(np.float32)
+    d = _dev(m)
+    g = gdr.mixer_epilogue_bwd(torch.from_numpy(o).cuda(), d["g"], d["norm_weight"],
+                               torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    go, gg, gw = mixer.epilogue_bwd(o, m["g"], m["norm_weight"], dy)
+    errs = {"d_o": rel_err(g["d_o"].cpu().numpy(), go), "dg": rel_err(g["dg"].cpu().numpy(), gg),
+            "dnorm_weight": rel_err(g["dnorm_weight"].cpu().numpy(), gw)}
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= BWD_TOL for e in errs.values()), errs
+
+
+def test_mixer_backward_deterministic():
+    """The tap and norm-weight gradients are summed in a fixed order."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    m = gs.mixer_inputs(2, 2, 300, 128, 128, seed=14)
+    d = _dev(m)
+    dy = torch.randn((2, 2, 300, 128), device="cuda")
+    a = gdr.mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], dy, dy, dy)
+    b = gdr.mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], dy, dy, dy)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_training_step_through_the_block():
+    """A whole training step of the token mixer on the GPU, gating fused:
+    prologue (q, k, v) -> forward on the gate logits -> epilogue, then the
+    epilogue's, the recurrence's and the prologue's backward, against the
+    oracle's composition of the same steps (its recurrence inputs and dO stored
+    in bf16 like the GPU's).  Each stage is held to its own tolerance by the
+    tests above and by the recurrence's tests; here their errors add up (the
+    forward's o error, amplified by the epilogue's per-row normalisation, then
+    the recurrence backward's own error, measured 3-7e-2 on the logits' and
+    projections' gradients), so this test checks that the stages compose:
+    layouts, the chain rule and the gate-logit convention.  A mistake in any
+    of those gives O(1) errors; the bound is 1e-1."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    B, H, T, D = 1, 2, 192, 128
+    print(f"mixer training step B={B} H={H} T={T} d={D}", flush=True)
+    m = gs.mixer_inputs(B, H, T, D, D, seed=15)
+    S0 = (np.random.default_rng(16).standard_normal((B, H, D, D)) * 0.02).astype(np.float32)
+    dy = np.random.default_rng(17).standard_normal((B, H, T, D)).astype(np.float32)
+    d = _dev(m)
+    S0d = torch.from_numpy(S0).cuda()
+    x = gdr.mixer_prologue(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"], d["conv_v"],
+                           d["a_pre"], d["b_pre"], d["w_pre"], gate_logits=True)
+    o, _ = gdr.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0d, chunk=64,
+                         gate_logits=True)
+    ge = gdr.mixer_epilogue_bwd(o, d["g"], d["norm_weight"], torch.from_numpy(dy).cuda())
+    gr = gdr.chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0d,
+                       ge["d_o"].to(torch.bfloat16), None, chunk=64, gate_logits=True)
+    gp = gdr.mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                                d["conv_v"], gr["dq"], gr["dk"], gr["dv"])
+    torch.cuda.synchronize()
+    # oracle composition
+    r = mixer.prologue(m["q_pre"], m["k_pre"], m["v_pre"], m["conv_q"], m["conv_k"], m["conv_v"],
+                       m["a_pre"], m["b_pre"], m["w_pre"])
+    qkv = {n: gs.bf16_round(r[n].astype(np.float32)) for n in ("q", "k", "v")}
+    o_ref, _ = oracle.fwd(qkv["q"], qkv["k"], qkv["v"], r["log_alpha"], r["b"], r["w"], S0)
+    go_ref, gg_ref, gw_ref = mixer.epilogue_bwd(o_ref, m["g"], m["norm_weight"], dy)
+    # the GPU hands the recurrence's backward dO in bf16: the oracle rounds its own
+    g_ref = oracle.bwd(qkv["q"], qkv["k"], qkv["v"], r["log_alpha"], r["b"], r["w"], S0,
+                       gs.bf16_round(go_ref.astype(np.float32)), None)
+    sa = mixer.sigmoid(-np.asarray(m["a_pre"], dtype=np.float64))
+    ref = {"dg": gg_ref, "dnorm_weight": gw_ref,
+           "da_pre": g_ref["dlog_alpha"] * sa,
+           "db_pre": g_ref["db"] * r["b"] * (1 - r["b"]),
+           "dw_pre": g_ref["dw"] * r["w"] * (1 - r["w"])}
+    for n, l2 in (("q", True), ("k", True), ("v", False)):
+        gx, gw = mixer.stream_bwd(m[f"{n}_pre"], m[f"conv_{n}"], g_ref[f"d{n}"], l2)
+        ref[f"d{n}_pre"], ref[f"dconv_{n}"] = gx, gw
+    got = {"dg": ge["dg"], "dnorm_weight": ge["dnorm_weight"], "da_pre": gr["dlog_alpha"],
+           "db_pre": gr["db"], "dw_pre": gr["dw"], "dq_pre": gp["dq_pre"], "dk_pre": gp["dk_pre"],
+           "dv_pre": gp["dv_pre"], "dconv_q": gp["dconv_q"], "dconv_k": gp["dconv_k"],
+           "dconv_v": gp["dconv_v"]}
+    errs = {n: rel_err(got[n].cpu().numpy(), ref[n]) for n in ref}
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= 1e-1 for e in errs.values()), errs
+    # the bound discriminates: the decay-logit gradient without its chain-rule
+    # factor sigmoid(-a) is far outside it
+    assert rel_err(got["da_pre"].cpu().numpy(), g_ref["dlog_alpha"]) > 0.5

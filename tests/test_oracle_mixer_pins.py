@@ -103,3 +103,54 @@ def test_epilogue_is_norm_times_gate():
     g_big = np.full(o.shape, 60.0)
     np.testing.assert_allclose(mixer.epilogue(o, g_big, wgt), mixer.rms_norm(o, wgt) * 60.0, rtol=1e-14)
     np.testing.assert_array_equal(mixer.epilogue(o, np.zeros(o.shape), wgt), 0.0)
+
+
+def _fd_check(f, inputs, cotangent, grads, seed, h=1e-6):
+    """Central differences of <cotangent, f(inputs)> along random directions,
+    against the inner product of the returned gradients with them."""
+    r = rng(seed)
+    for _ in range(3):
+        dirs = [r.standard_normal(np.shape(x)) for x in inputs]
+        plus = [x + h * d for x, d in zip(inputs, dirs)]
+        minus = [x - h * d for x, d in zip(inputs, dirs)]
+        fd = (np.sum(cotangent * f(*plus)) - np.sum(cotangent * f(*minus))) / (2 * h)
+        an = sum(np.sum(gr * d) for gr, d in zip(grads, dirs))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("l2", [True, False])
+def test_stream_backward_finite_differences(l2):
+    """Reverse mode of conv -> SiLU (-> L2 norm) against central differences
+    of the forward (which the autograd path does not use)."""
+    H, T, D = 2, 9, 6
+    x = _x((1, H, T, D), 11)
+    taps = _x((H, D, mixer.TAPS), 12) * 0.5
+    dy = _x((1, H, T, D), 13)
+    gx, gw = mixer.stream_bwd(x, taps, dy, l2)
+    assert gx.shape == x.shape and gw.shape == taps.shape
+
+    def f(x_, w_):
+        y = mixer.silu(mixer.causal_conv(x_, w_))
+        return mixer.l2norm(y) if l2 else y
+    _fd_check(f, [x, taps], dy, [gx, gw], 14)
+
+
+def test_epilogue_backward_finite_differences():
+    o = _x((1, 2, 5, 8), 15)
+    g = _x((1, 2, 5, 8), 16)
+    wgt = 1.0 + 0.1 * _x((8,), 17)
+    dy = _x((1, 2, 5, 8), 18)
+    go, gg, gw = mixer.epilogue_bwd(o, g, wgt, dy)
+    _fd_check(mixer.epilogue, [o, g, wgt], dy, [go, gg, gw], 19)
+
+
+def test_stream_backward_is_anticausal():
+    """The gradient of token t's input collects only outputs t .. t+3."""
+    H, T, D = 1, 12, 4
+    x = _x((1, H, T, D), 20)
+    taps = _x((H, D, mixer.TAPS), 21)
+    dy = np.zeros((1, H, T, D))
+    dy[..., 6, :] = 1.0
+    gx, _ = mixer.stream_bwd(x, taps, dy, False)
+    assert np.all(gx[..., 7:, :] == 0.0) and np.all(gx[..., :3, :] == 0.0)
+    assert np.all(np.abs(gx[..., 3:7, :]).max(axis=-1) > 0)
