@@ -190,3 +190,40 @@ def test_packed_backward_workload_shape_sampled():
     inp = _case("workload", lengths, H=16, dk=128, dv=128, seed=5)
     dSf = _dsf(inp)
     _check(inp, _run(inp, dSf), _oracle(inp, dSf, heads=heads), heads=heads)
+
+
+def test_packed_calls_replay_from_a_graph():
+    """The packed forward and backward (prep kernels, the two chains on two
+    streams) captured into one graph replay to the eager results, bit for bit,
+    on several replays with eager work between them."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    inp = _case("graph", [5, 64, 130, 0, 77], H=2, dk=128, dv=128)
+    d = _dev(inp)
+    dsf = torch.from_numpy(_dsf(inp)).cuda()
+
+    def run():
+        o, sf = gdr.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["cu"],
+                                     d["S0"])
+        g = gdr.chunk_bwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["cu"],
+                                 d["S0"], d["dO"], dsf)
+        return dict(o=o, sf=sf, **g)
+    eager = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        x = torch.randn(1 << 20, device="cuda")
+        x.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in eager:
+            assert torch.equal(captured[n], eager[n]), (rep, n)

@@ -264,3 +264,36 @@ def test_training_step_through_the_block():
     # the bound discriminates: the decay-logit gradient without its chain-rule
     # factor sigmoid(-a) is far outside it
     assert rel_err(got["da_pre"].cpu().numpy(), g_ref["dlog_alpha"]) > 0.5
+
+
+def test_mixer_calls_replay_from_a_graph():
+    """Prologue, epilogue and their backward (with the deterministic
+    reductions) captured into one graph replay to the eager results."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    m = gs.mixer_inputs(1, 2, 200, 128, 128, seed=21)
+    d = _dev(m)
+    o = torch.randn((1, 2, 200, 128), device="cuda")
+    dy = torch.randn((1, 2, 200, 128), device="cuda")
+
+    def run():
+        x = gdr.mixer_prologue(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                               d["conv_v"], d["a_pre"], d["b_pre"], d["w_pre"])
+        y = gdr.mixer_epilogue(o, d["g"], d["norm_weight"])
+        gp = gdr.mixer_prologue_bwd(d["q_pre"], d["k_pre"], d["v_pre"], d["conv_q"], d["conv_k"],
+                                    d["conv_v"], dy, dy, dy)
+        ge = gdr.mixer_epilogue_bwd(o, d["g"], d["norm_weight"], dy)
+        return dict(y=y, **x, **gp, **ge)
+    eager = run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        x = torch.randn(1 << 20, device="cuda")
+        x.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in eager:
+            assert torch.equal(captured[n], eager[n]), (rep, n)
