@@ -181,11 +181,11 @@ def test_equal_lengths_match_fixed_length_backward():
     _check(inp, got, _oracle(inp, dSf))
 
 
-def test_packed_backward_workload_shape_sampled():
+def test_packed_backward_workload_shape_all_heads():
     """Eight documents per head row with long-tailed lengths around 2048
-    tokens (about 16K tokens per head, 16 heads, d=128): every gradient on
-    three sampled heads against the oracle."""
-    heads = [0, 9, 15]
+    tokens (about 16K tokens per head, 16 heads, d=128): every gradient of
+    every head against the oracle."""
+    heads = list(range(16))
     lengths = gs.packed_lengths(8, 2048, seed=5)
     inp = _case("workload", lengths, H=16, dk=128, dv=128, seed=5)
     dSf = _dsf(inp)

@@ -237,19 +237,19 @@ def test_decay_beyond_f16_range_is_loud(path):
     assert torch.isnan(o).any()
 
 
-def test_gdn2_full_workload_sampled_heads():
+def test_gdn2_full_workload_all_heads():
     """Gated DeltaNet-2 at B=2, H=16, T=8192, d=128, chunk 64 (the timed
-    launch), compared on 4 sampled heads."""
+    launch), every output of every head against the oracle."""
     inp = _case("gdn2")
     o, sf = _run(inp)
-    _check(inp, o, sf, 2e-2, heads=[0, 7, 21, 31])
+    _check(inp, o, sf, 2e-2)
 
 
-def test_gdn_full_workload_sampled_heads():
-    """Gated DeltaNet (scalar gates) at B=4, H=16, T=2048, d=128."""
+def test_gdn_full_workload_all_heads():
+    """Gated DeltaNet (scalar gates) at B=4, H=16, T=2048, d=128, every head."""
     inp = _case("gdn")
     o, sf = _run(inp)
-    _check(inp, o, sf, 2e-2, heads=[0, 13, 40, 63])
+    _check(inp, o, sf, 2e-2)
 
 
 
