@@ -842,16 +842,11 @@ static hipError_t launch_t(const BwdParams& p, hipStream_t st, bool with_dstate)
     using LG = GradLayout<DK, DV, C, F32>;
     auto kd = dstate_kernel<DK, DV, C, F32>;
     auto kg = grad_kernel<DK, DV, C, F32>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kd),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LD::bytes);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kg),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LG::bytes);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<unsigned long long> done_d{0}, done_g{0};
+    hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kd), (int)LD::bytes, done_d);
+    if (e != hipSuccess) return e;
+    e = ensure_dyn_lds(reinterpret_cast<const void*>(kg), (int)LG::bytes, done_g);
+    if (e != hipSuccess) return e;
     const int NC = p.T / C;
     if (with_dstate) {
         hipLaunchKernelGGL(kd, dim3((unsigned)(p.BH * (DV / VB))), dim3(LD::NT), LD::bytes, st, p);

@@ -851,14 +851,9 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
 template <int D, bool AS, bool BS, bool WS, bool VL, bool LG>
 static hipError_t launch_wgrad_v(const BwdParams& p, const void* ws, hipStream_t st) {
     auto k = wgrad_kernel<D, AS, BS, WS, VL, LG>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)WgradLayout<D>::bytes);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<unsigned long long> done{0};
+    const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(k), (int)WgradLayout<D>::bytes, done);
+    if (e != hipSuccess) return e;
     // packed sequences: the chunk count is on the device; the grid covers the
     // largest possible count and the workgroups past the real one return at once
     const size_t items = VL ? (size_t)p.BH * packed_max_chunks(p.T, p.nseq) : (size_t)p.BH * (p.T / C);

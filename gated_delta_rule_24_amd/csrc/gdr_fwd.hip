@@ -486,13 +486,9 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t st) {
     constexpr int VB = pick_vb<DK, DV, C, F32>();
     using L = FwdLayout<DK, DV, C, VB, F32>;
     auto kern = fwd_kernel<DK, DV, C, VB, F32>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<unsigned long long> done{0};
+    const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kern), (int)L::bytes, done);
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)(p.BH * (DV / VB))), block(256);
     hipLaunchKernelGGL(kern, grid, block, L::bytes, st, p);
     return hipGetLastError();

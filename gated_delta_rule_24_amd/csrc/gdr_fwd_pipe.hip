@@ -613,13 +613,9 @@ template <int DK, int DV, bool AS, bool BS, bool WS>
 static hipError_t launch_t(const FwdParams& p, hipStream_t st) {
     using L = Layout<DK>;
     auto kern = fwd_pipe_kernel<DK, DV, AS, BS, WS>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<unsigned long long> done{0};
+    const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kern), (int)L::bytes, done);
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)(p.BH * (DV / VB))), block(64 * (NCW + NPW));
     hipLaunchKernelGGL(kern, grid, block, L::bytes, st, p);
     return hipGetLastError();

@@ -957,12 +957,10 @@ static hipError_t launch_t(const FwdParams& p, void* ws, hipStream_t st, int pas
     auto kp = lg ? wy_kernel<DK, DV, AS, BS, WS, BL, VL, true> : wy_kernel<DK, DV, AS, BS, WS, BL, VL, false>;
     auto ks = chain_kernel<DK, DV, kChainStrips, VL>;
     constexpr size_t RB = BL ? Rec<DK, DV>::bwd_bytes : Rec<DK, DV>::bytes;
-    static bool attr_done[2] = {false, false};
-    if (!attr_done[lg]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::bytes);
+    static std::atomic<unsigned long long> done[2];
+    {
+        const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kp), (int)LP::bytes, done[lg]);
         if (e != hipSuccess) return e;
-        attr_done[lg] = true;
     }
     // (packed sequences: the chunk count is on the device; the WY grid is one
     // workgroup per compute unit)

@@ -2,6 +2,8 @@
 // translation units.  Not installed; callers use include/gdr.h.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -9,6 +11,21 @@
 #include "../../include/gdr.h"
 
 namespace gdr {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device: the setting
+// belongs to the function on the current device, so a process that uses
+// several GPUs sets it on each.  `done` keeps one bit per device (devices
+// numbered 64 and up set it on every launch); safe to call from several threads.
+inline hipError_t ensure_dyn_lds(const void* fn, int bytes, std::atomic<unsigned long long>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 struct DecodeParams {
     const void* q;
