@@ -63,7 +63,7 @@ extern "C" {
 typedef enum gdr_status {
     GDR_OK = 0,
     GDR_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misalignment, T % chunk != 0 */
-    GDR_ERR_UNSUPPORTED = 2,     /* a valid request this build has no kernel for      */
+    GDR_ERR_UNSUPPORTED = 2,     /* a valid request the library has no kernel for     */
     GDR_ERR_WORKSPACE = 3,       /* workspace pointer NULL or smaller than required   */
     GDR_ERR_LAUNCH = 4,          /* the HIP runtime rejected a launch                 */
     GDR_ERR_DEVICE = 5           /* no usable gfx950 device / device query failed     */
