@@ -22,6 +22,8 @@
 // D/8 lanes of one wave (8 channels, one 16-byte access per lane), so the
 // per-token norms are lane shuffles.
 #include "gdr_device.h"
+#include <type_traits>
+
 #include "gdr_launch.h"
 
 namespace gdr {
@@ -246,82 +248,105 @@ __global__ __launch_bounds__(NT) void epilogue_kernel(EpilogueParams p) {
 //   dc = ds * SiLU'(c),  SiLU'(c) = sigmoid(c) (1 + c (1 - sigmoid(c)))
 //   dx_t = sum_j w_j dc_{t+j}        (the transposed, anti-causal convolution)
 //   dw_j = sum_t dc_t x_{t-j}        (over all tokens of all sequences of the head)
-// Each thread takes BTPT consecutive tokens of 8 channels and recomputes c for
+// Each thread takes BTPT consecutive tokens of CPL channels and recomputes c for
 // them and the 3 tokens after them (whose dc its dx needs).  dw is summed per
 // workgroup in LDS, written as one partial per (sequence, tile), and the
 // partials are added in a fixed order by reduce_taps (deterministic).
 constexpr int BTILE = 64;     // tokens per prologue-backward workgroup
+// channels per lane: 4 rather than the forward's 8 halves the per-token
+// register arrays (3 waves per SIMD instead of 2 at d = 128) and, with twice the
+// lanes per token, gives each thread twice the tokens, so fewer halo tokens are
+// recomputed (11 per 8 tokens instead of 7 per 4)
+constexpr int kBwdCPL = 4;
 
 __device__ __forceinline__ float silu_grad(float c) {
     const float sg = gate_sigmoid(c);
     return sg * (1.f + c * (1.f - sg));
 }
 
-template <int D, bool L2>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// CPL bf16 values (CPL = 4 or 8) packed two per 32-bit word, to fp32
+template <int CPL, typename V>
+__device__ __forceinline__ void unpack_n(V u, float (&f)[CPL]) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+
+template <int D, bool L2, int CPL = kBwdCPL>
 __device__ __forceinline__ void stream_bwd_tile(const uint16_t* src, const float* taps, const float* dy, float* dx,
                                                 float* part, int h, size_t bh, int T, int t0) {
-    constexpr int LPT = D / 8, BTPT = BTILE * LPT / NT;
+    static_assert(CPL == 4 || CPL == 8, "channels per lane");
+    using Raw = typename std::conditional<CPL == 8, u32x4, u32x2>::type;
+    constexpr int LPT = D / CPL, BTPT = BTILE * LPT / NT, NQ = CPL / 4;
     constexpr int NU = BTPT + kConvTaps - 1;        // tokens whose dc this thread forms
     constexpr int NR = NU + kConvTaps - 1;          // input rows it reads
     static_assert(BTPT * NT == BTILE * LPT && 64 % LPT == 0, "token mapping");
     __shared__ floatx4 sW[NT / 64][D];              // per wave: dw partial per channel
     const int tid = threadIdx.x, co = tid % LPT, tl = tid / LPT;
-    floatx4 w[8];
+    floatx4 w[CPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        w[c] = *reinterpret_cast<const floatx4*>(taps + ((size_t)h * D + 8 * co + c) * kConvTaps);
-    const size_t base = bh * (size_t)T * D + 8 * co;
+    for (int c = 0; c < CPL; ++c)
+        w[c] = *reinterpret_cast<const floatx4*>(taps + ((size_t)h * D + CPL * co + c) * kConvTaps);
+    const size_t base = bh * (size_t)T * D + CPL * co;
     const int ta = t0 + tl * BTPT;
     // input rows ta-3 .. ta+NU-1 (zero outside the sequence)
-    u32x4 raw[NR];
+    Raw raw[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int t = ta - (kConvTaps - 1) + r;
         const bool in = t >= 0 && t < T;
-        raw[r] = *reinterpret_cast<const u32x4*>(src + base + (size_t)(in ? t : 0) * D);
-        if (!in) raw[r] = u32x4{0u, 0u, 0u, 0u};
+        raw[r] = *reinterpret_cast<const Raw*>(src + base + (size_t)(in ? t : 0) * D);
+        if (!in) raw[r] = Raw{};
     }
     // gradients of this thread's tokens (loaded up front), zero past the end
-    floatx4 gy[NU][2];
+    floatx4 gy[NU][NQ];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
         const int t = ta + u;
         const bool in = t < T;
-        gy[u][0] = *reinterpret_cast<const floatx4*>(dy + base + (size_t)(in ? t : 0) * D);
-        gy[u][1] = *reinterpret_cast<const floatx4*>(dy + base + (size_t)(in ? t : 0) * D + 4);
-        if (!in) gy[u][0] = gy[u][1] = zero4();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            gy[u][q] = *reinterpret_cast<const floatx4*>(dy + base + (size_t)(in ? t : 0) * D + 4 * q);
+            if (!in) gy[u][q] = zero4();
+        }
     }
     // dc of tokens ta .. ta+NU-1, one token at a time, each added at once into
     // dx of the tokens it reaches (ta+u-j for tap j) and, for this thread's own
     // tokens, into dw
-    float dxa[BTPT][8];
+    float dxa[BTPT][CPL];
 #pragma unroll
     for (int i2 = 0; i2 < BTPT; ++i2)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dxa[i2][c] = 0.f;
-    floatx4 dw[8];
+        for (int c = 0; c < CPL; ++c) dxa[i2][c] = 0.f;
+    floatx4 dw[CPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) dw[c] = zero4();
+    for (int c = 0; c < CPL; ++c) dw[c] = zero4();
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        float g[8], cv[8], sl[8], dcu[8];
+        float g[CPL], cv[CPL], sl[CPL], dcu[CPL];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { g[c] = gy[u][0][c]; g[c + 4] = gy[u][1][c]; }
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) cv[c] = 0.f;
+            for (int c = 0; c < 4; ++c) g[4 * q + c] = gy[u][q][c];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) cv[c] = 0.f;
 #pragma unroll
         for (int j = 0; j < kConvTaps; ++j) {
-            float x[8];
-            unpack8(raw[u + kConvTaps - 1 - j], x);
+            float x[CPL];
+            unpack_n<CPL>(raw[u + kConvTaps - 1 - j], x);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) cv[c] += w[c][j] * x[c];
+            for (int c = 0; c < CPL; ++c) cv[c] += w[c][j] * x[c];
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sl[c] = silu(cv[c]);
+        for (int c = 0; c < CPL; ++c) sl[c] = silu(cv[c]);
         if constexpr (L2) {
             float ss = 0.f, sd = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) { ss += sl[c] * sl[c]; sd += sl[c] * g[c]; }
+            for (int c = 0; c < CPL; ++c) { ss += sl[c] * sl[c]; sd += sl[c] * g[c]; }
 #pragma unroll
             for (int off = 1; off < LPT; off *= 2) {
                 ss += __shfl_xor(ss, off, 64);
@@ -329,25 +354,25 @@ __device__ __forceinline__ void stream_bwd_tile(const uint16_t* src, const float
             }
             const float r = rsqrtf(ss + kEps), r3sd = r * r * r * sd;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) g[c] = r * g[c] - r3sd * sl[c];
+            for (int c = 0; c < CPL; ++c) g[c] = r * g[c] - r3sd * sl[c];
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dcu[c] = g[c] * silu_grad(cv[c]);
+        for (int c = 0; c < CPL; ++c) dcu[c] = g[c] * silu_grad(cv[c]);
 #pragma unroll
         for (int j = 0; j < kConvTaps; ++j) {
             const int i2 = u - j;                   // dx of token ta+i2 takes w_j dc_{ta+u}
             if (i2 >= 0 && i2 < BTPT) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) dxa[i2][c] += w[c][j] * dcu[c];
+                for (int c = 0; c < CPL; ++c) dxa[i2][c] += w[c][j] * dcu[c];
             }
         }
         if (u < BTPT && ta + u < T) {
 #pragma unroll
             for (int j = 0; j < kConvTaps; ++j) {
-                float x[8];
-                unpack8(raw[u + kConvTaps - 1 - j], x);
+                float x[CPL];
+                unpack_n<CPL>(raw[u + kConvTaps - 1 - j], x);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) dw[c][j] += dcu[c] * x[c];
+                for (int c = 0; c < CPL; ++c) dw[c][j] += dcu[c] * x[c];
             }
         }
     }
@@ -355,10 +380,10 @@ __device__ __forceinline__ void stream_bwd_tile(const uint16_t* src, const float
     for (int i2 = 0; i2 < BTPT; ++i2) {
         const int t = ta + i2;
         if (t < T) {
-            *reinterpret_cast<floatx4*>(dx + base + (size_t)t * D) =
-                floatx4{dxa[i2][0], dxa[i2][1], dxa[i2][2], dxa[i2][3]};
-            *reinterpret_cast<floatx4*>(dx + base + (size_t)t * D + 4) =
-                floatx4{dxa[i2][4], dxa[i2][5], dxa[i2][6], dxa[i2][7]};
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                *reinterpret_cast<floatx4*>(dx + base + (size_t)t * D + 4 * q) =
+                    floatx4{dxa[i2][4 * q], dxa[i2][4 * q + 1], dxa[i2][4 * q + 2], dxa[i2][4 * q + 3]};
         }
     }
     // over the token groups of the wave (lanes LPT apart hold the same channels),
@@ -366,12 +391,12 @@ __device__ __forceinline__ void stream_bwd_tile(const uint16_t* src, const float
 #pragma unroll
     for (int off = LPT; off < 64; off *= 2)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < CPL; ++i)
 #pragma unroll
             for (int j = 0; j < kConvTaps; ++j) dw[i][j] += __shfl_xor(dw[i][j], off, 64);
     if ((tid & 63) < LPT) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sW[tid >> 6][8 * co + i] = dw[i];
+        for (int i = 0; i < CPL; ++i) sW[tid >> 6][CPL * co + i] = dw[i];
     }
     __syncthreads();
     for (int c = tid; c < D; c += NT) {
