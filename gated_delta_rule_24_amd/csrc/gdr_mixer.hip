@@ -55,68 +55,92 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
     return u;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// CPL bf16 values (CPL = 4 or 8) packed two per 32-bit word, to fp32
+template <int CPL, typename V>
+__device__ __forceinline__ void unpack_n(V u, float (&f)[CPL]) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+
+// channels per lane in the forward convolution tiles (4 measured slightly slower:
+// its 8-byte accesses cost more than the shorter halo saves)
+constexpr int kFwdCPL = 8;
+
 // conv, SiLU and (L2) the L2 norm of tokens t0 .. t0+TILE-1 of stream bh (head h).
-// Each thread takes TPT consecutive tokens of 8 channels: it loads them and the
+// Each thread takes TPT consecutive tokens of CPL channels: it loads them and the
 // kConvTaps-1 tokens before them once (a sliding window in registers), so each
 // input row passes the memory pipeline (TPT + 3) / TPT times, not kConvTaps times.
-template <int D, bool L2>
+template <int D, bool L2, int CPL = kFwdCPL>
 __device__ __forceinline__ void conv_tile(const uint16_t* src, const float* taps, uint16_t* dst, int h, size_t bh,
                                           int T, int t0) {
-    constexpr int LPT = D / 8;                  // lanes per token
+    static_assert(CPL == 4 || CPL == 8, "channels per lane");
+    using Raw = typename std::conditional<CPL == 8, u32x4, u32x2>::type;
+    constexpr int LPT = D / CPL;                // lanes per token
     constexpr int TPT = TILE * LPT / NT;        // consecutive tokens per thread
     constexpr int NR = TPT + kConvTaps - 1;     // rows a thread reads
     static_assert(TPT * NT == TILE * LPT && 64 % LPT == 0, "token mapping");
     const int tid = threadIdx.x, co = tid % LPT, tl = tid / LPT;
-    floatx4 w[8];
+    floatx4 w[CPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        w[c] = *reinterpret_cast<const floatx4*>(taps + ((size_t)h * D + 8 * co + c) * kConvTaps);
-    const uint16_t* s = src + bh * (size_t)T * D + 8 * co;
-    uint16_t* d = dst + bh * (size_t)T * D + 8 * co;
+    for (int c = 0; c < CPL; ++c)
+        w[c] = *reinterpret_cast<const floatx4*>(taps + ((size_t)h * D + CPL * co + c) * kConvTaps);
+    const uint16_t* s = src + bh * (size_t)T * D + CPL * co;
+    uint16_t* d = dst + bh * (size_t)T * D + CPL * co;
     const int ta = t0 + tl * TPT;               // this thread's first token
     // rows ta-3 .. ta+TPT-1; rows before the sequence or past its end read as zero
-    u32x4 raw[NR];
+    Raw raw[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int t = ta - (kConvTaps - 1) + r;
         const bool in = t >= 0 && t < T;
-        raw[r] = *reinterpret_cast<const u32x4*>(s + (size_t)(in ? t : 0) * D);
-        if (!in) raw[r] = u32x4{0u, 0u, 0u, 0u};
+        raw[r] = *reinterpret_cast<const Raw*>(s + (size_t)(in ? t : 0) * D);
+        if (!in) raw[r] = Raw{};
     }
-    float acc[TPT][8];
+    float acc[TPT][CPL];
 #pragma unroll
     for (int i = 0; i < TPT; ++i)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
+        for (int c = 0; c < CPL; ++c) acc[i][c] = 0.f;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        float x[8];
-        unpack8(raw[r], x);
+        float x[CPL];
+        unpack_n<CPL>(raw[r], x);
         // row r is token ta + r - 3: it is tap j of output i = r - 3 + j
 #pragma unroll
         for (int j = 0; j < kConvTaps; ++j) {
             const int i = r - (kConvTaps - 1) + j;
             if (i >= 0 && i < TPT) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[i][c] += w[c][j] * x[c];
+                for (int c = 0; c < CPL; ++c) acc[i][c] += w[c][j] * x[c];
             }
         }
     }
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[i][c] = silu(acc[i][c]);
+        for (int c = 0; c < CPL; ++c) acc[i][c] = silu(acc[i][c]);
         if constexpr (L2) {
             float ss = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) ss += acc[i][c] * acc[i][c];
+            for (int c = 0; c < CPL; ++c) ss += acc[i][c] * acc[i][c];
 #pragma unroll
             for (int off = 1; off < LPT; off *= 2) ss += __shfl_xor(ss, off, 64);
             const float sc = rsqrtf(ss + kEps);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[i][c] *= sc;
+            for (int c = 0; c < CPL; ++c) acc[i][c] *= sc;
         }
-        if (ta + i < T) *reinterpret_cast<u32x4*>(d + (size_t)(ta + i) * D) = pack8(acc[i]);
+        if (ta + i < T) {
+            Raw o;
+#pragma unroll
+            for (int c = 0; c < CPL / 2; ++c)
+                o[c] = (uint32_t)f32_to_bf16(acc[i][2 * c]) | ((uint32_t)f32_to_bf16(acc[i][2 * c + 1]) << 16);
+            *reinterpret_cast<Raw*>(d + (size_t)(ta + i) * D) = o;
+        }
     }
 }
 
@@ -262,18 +286,6 @@ constexpr int kBwdCPL = 4;
 __device__ __forceinline__ float silu_grad(float c) {
     const float sg = gate_sigmoid(c);
     return sg * (1.f + c * (1.f - sg));
-}
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// CPL bf16 values (CPL = 4 or 8) packed two per 32-bit word, to fp32
-template <int CPL, typename V>
-__device__ __forceinline__ void unpack_n(V u, float (&f)[CPL]) {
-#pragma unroll
-    for (int i = 0; i < CPL / 2; ++i) {
-        f[2 * i] = __uint_as_float(u[i] << 16);
-        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
 }
 
 template <int D, bool L2, int CPL = kBwdCPL>
