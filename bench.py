@@ -48,6 +48,13 @@ FWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
 # in-chunk products 2C(3 d_k + 2 d_v)
 FWD_FLOPS_PER_TOKEN = 6 * FD * FD + 2 * FC * (3 * FD + 2 * FD)
 
+# Gated DeltaNet workload (scalar decay, one tied scalar beta as b and w, no
+# S0): B=4 H=16 T=2048 d=128 chunk 64; algorithmic bytes per head-token: q, k,
+# v bf16 + log-decay fp32 (one per token) + beta bf16 (one per token) + o fp32,
+# plus S_final written once per head
+GDN_BYTES_PER_TOKEN = 3 * FD * 2 + 4 + 2 + FD * 4
+GDN_STATE_BYTES_PER_HEAD = FD * FD * 4
+
 # decode workload
 DN, DH, DD = 256, 32, 128
 SMALL_DECODE_N = (1, 16)          # small-batch (latency) decode lines
@@ -130,8 +137,9 @@ def upload(inp):
 
 
 def time_loop(fn, steps, warmup):
-    """Average wall ms and event ms per call over `steps` timed calls; the
-    events are recorded on torch's current stream, where libgdr launches."""
+    """Average wall ms and event ms per call over `steps` back-to-back timed
+    calls; the events are recorded on torch's current stream, where libgdr
+    launches."""
     import torch
     for _ in range(warmup):
         fn()
@@ -148,23 +156,66 @@ def time_loop(fn, steps, warmup):
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
-def bench_fwd(steps, warmup):
+_FLUSH = []
+
+
+def time_cold(fn, steps):
+    """Per-call event ms with the caches emptied before each call: a 1 GiB
+    buffer (four times the 256 MiB Infinity Cache) is read outside the event
+    window, so every call starts from HBM.  The flush reads rather than
+    writes: written lines would stay dirty in the caches and be written back
+    inside the next call's window.  Returns (median, min, max)."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.zeros(1 << 28, dtype=torch.float32, device="cuda"))
+    buf = _FLUSH[0]
+    evs = []
+    for i in range(steps):
+        buf.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms[len(ms) // 2], ms[0], ms[-1]
+
+
+def cold_stats(fn, steps, nbytes=None):
+    """The cold-call (cache-flushed) median and range of one call, in us, and
+    the rate of its algorithmic bytes at the median."""
+    med, lo, hi = time_cold(fn, steps)
+    out = {"cold_median_us": med * 1e3, "cold_min_us": lo * 1e3, "cold_max_us": hi * 1e3,
+           "cold_calls": steps}
+    if nbytes is not None:
+        out["cold_GB_per_s"] = nbytes / (med * 1e-3) / 1e9
+        out["cold_frac_hbm_peak"] = nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return out
+
+
+def bench_fwd(steps, warmup, name="gdn2"):
+    """One gdr_chunk_fwd call per step on the named synthetic workload
+    (gdn2: B=2 H=16 T=8192 channel gates; gdn: B=4 H=16 T=2048 scalar decay,
+    tied scalar beta, no S0)."""
     import torch
     import gdr_synth as gs
     import gated_delta_rule_24_amd as gdr
-    inp = gs.preset("gdn2", seed=0)
+    inp = gs.preset(name, seed=0)
     d = upload(inp)
-    o = torch.empty((FB, FH, FT, FD), dtype=torch.float32, device="cuda")
-    Sf = torch.empty((FB, FH, FD, FD), dtype=torch.float32, device="cuda")
+    B, H, T, dk, dv, C = inp.B, inp.H, inp.T, inp.dk, inp.dv, inp.chunk
+    o = torch.empty((B, H, T, dv), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
     flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
-    nbytes = gdr.gdr_chunk_fwd_workspace_bytes(FB, FH, FT, FD, FD, FC, flags)
+    nbytes = gdr.gdr_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, flags)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
 
     def step():
         gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], o, Sf,
-                          FB, FH, FT, FD, FD, FC, flags, ws, nbytes)
+                          B, H, T, dk, dv, C, flags, ws, nbytes)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
-    return inp, wall_ms, ev_ms
+    return inp, wall_ms, ev_ms, step
 
 
 def bench_decode(steps, warmup, N=None, graph=False):
@@ -192,7 +243,7 @@ def bench_decode(steps, warmup, N=None, graph=False):
                             N, DH, DD, DD, 0)
     if not graph:
         wall_ms, ev_ms = time_loop(step, steps, warmup)
-        return wall_ms, ev_ms
+        return wall_ms, ev_ms, step
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -243,7 +294,7 @@ def bench_varlen(steps, warmup):
         gdr.gdr_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0, o,
                                  Sf, cu, nseq, VH, VT, FD, FD, flags, ws, nbytes)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
-    return lengths, wall_ms, ev_ms
+    return lengths, wall_ms, ev_ms, step
 
 
 def bench_bwd_varlen(steps, warmup):
@@ -274,7 +325,7 @@ def bench_bwd_varlen(steps, warmup):
                                  d["dO"], None, g["dq"], g["dk"], g["dv"], g["dla"], g["db"],
                                  g["dw"], dS0, cu, nseq, BH_, VT, FD, FD, flags, ws, nbytes)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
-    return lengths, wall_ms, ev_ms
+    return lengths, wall_ms, ev_ms, step
 
 
 def bench_mixer(steps, warmup):
@@ -370,12 +421,25 @@ def bench_bwd(steps, warmup):
                           None, g["dq"], g["dk"], g["dv"], g["dla"], g["db"], g["dw"], dS0,
                           BB, BH_, BT, FD, FD, FC, flags, ws, nbytes)
     wall_ms, ev_ms = time_loop(step, steps, warmup)
-    return wall_ms, ev_ms, nbytes
+    return wall_ms, ev_ms, nbytes, step
 
 
-def cpu_baseline(inp, min_seconds=10.0, max_passes=50):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, min_seconds=10.0, max_passes=50, one_thread_seconds=4.0):
     """The fp64 oracle on this host over the same GDN-2 workload, repeated
-    until about `min_seconds` of CPU work have been timed."""
+    until about `min_seconds` of CPU work have been timed with all cores
+    (OpenMP over the heads), then on one thread over the first head's first
+    tokens for about `one_thread_seconds`."""
     import oracle
     a = inp.arrays
     sel = lambda x: x.reshape((FB * FH,) + x.shape[2:])
@@ -388,10 +452,23 @@ def cpu_baseline(inp, min_seconds=10.0, max_passes=50):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= max_passes:
             break
+    # one thread: one head, 2048 tokens per pass
+    one = [x[:1] for x in args]
+    one = [x[:, :2048] if i < 6 else x for i, x in enumerate(one)]
+    p1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.fwd(*one, nthreads=1)
+        p1 += 1
+        dt1 = time.perf_counter() - t1
+        if dt1 >= one_thread_seconds:
+            break
     return dict(value=passes * FB * FH * FT / dt, unit="tokens/s", cores=oracle.num_threads(),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(), nproc=os.cpu_count(),
+                value_1thread=p1 * 2048 / dt1,
                 sample=f"full workload ({FB * FH} heads x {FT} tokens, d=128), {passes} passes of "
-                       f"the fp64 token recurrence, OpenMP over heads, {dt:.1f} s wall")
+                       f"the fp64 token recurrence, OpenMP over heads, {dt:.1f} s wall; "
+                       f"value_1thread: one head x 2048 tokens on one thread, {p1} passes, "
+                       f"{dt1:.1f} s wall")
 
 
 def main():
@@ -399,7 +476,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy", "varlen", "bwd_varlen", "mixer"],
+    ap.add_argument("--only", choices=["fwd", "gdn", "decode", "bwd", "copy", "varlen", "bwd_varlen",
+                                       "mixer"],
                     default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -421,16 +499,16 @@ def main():
         log(f"copy 1 GiB: {e:.3f} ms/launch, {2 * (1 << 30) / e / 1e6:.1f} GB/s")
         return
     if args.only == "decode":
-        w, e = bench_decode(args.steps, args.warmup)
+        w, e, _ = bench_decode(args.steps, args.warmup)
         log(f"decode: {e * 1e3:.1f} us/step, {DN * DH * DEC_BYTES_PER_HEAD / e / 1e6:.1f} GB/s")
         return
     if args.only == "varlen":
-        lengths, w, e = bench_varlen(args.steps, args.warmup)
+        lengths, w, e, _ = bench_varlen(args.steps, args.warmup)
         log(f"varlen fwd ({len(lengths)} sequences): {e * 1e3:.1f} us/step")
         return
     bwd_bytes = BB * BH_ * BT * BWD_BYTES_PER_TOKEN + BB * BH_ * BWD_STATE_BYTES_PER_HEAD
     if args.only == "bwd":
-        w, e, _ = bench_bwd(args.steps, args.warmup)
+        w, e, _, _ = bench_bwd(args.steps, args.warmup)
         log(f"bwd: {e * 1e3:.1f} us/step, {bwd_bytes / e / 1e6:.1f} GB/s")
         return
     if args.only == "mixer":
@@ -440,11 +518,15 @@ def main():
             f"{pbm * 1e3:.1f} us, epilogue backward {ebm * 1e3:.1f} us")
         return
     if args.only == "bwd_varlen":
-        lengths, w, e = bench_bwd_varlen(args.steps, args.warmup)
+        lengths, w, e, _ = bench_bwd_varlen(args.steps, args.warmup)
         log(f"bwd varlen ({len(lengths)} sequences): {e * 1e3:.1f} us/step")
         return
 
-    inp, wall_ms, ev_ms = bench_fwd(args.steps, args.warmup)
+    if args.only == "gdn":
+        inp, w, e, _ = bench_fwd(args.steps, args.warmup, "gdn")
+        log(f"gdn fwd: {e * 1e3:.1f} us/step")
+        return
+    inp, wall_ms, ev_ms, fwd_step = bench_fwd(args.steps, args.warmup)
     ntok = FB * FH * FT
     fwd_bytes = ntok * FWD_BYTES_PER_TOKEN + FB * FH * FWD_STATE_BYTES_PER_HEAD
     fwd_flops = ntok * FWD_FLOPS_PER_TOKEN
@@ -454,19 +536,31 @@ def main():
     if args.only == "fwd":
         return
 
-    dec_wall, dec_ev = bench_decode(max(args.steps, 10), args.warmup)
+    fwd_cold = cold_stats(fwd_step, args.steps, fwd_bytes)
+    log(f"fwd cold (caches flushed before each call): median {fwd_cold['cold_median_us']:.1f} us")
+
+    # Gated DeltaNet (scalar decay, tied scalar beta): B=4 H=16 T=2048
+    ginp, g_wall, g_ev, g_step = bench_fwd(args.steps, args.warmup, "gdn")
+    g_ntok = ginp.B * ginp.H * ginp.T
+    g_bytes = g_ntok * GDN_BYTES_PER_TOKEN + ginp.B * ginp.H * GDN_STATE_BYTES_PER_HEAD
+    g_cold = cold_stats(g_step, args.steps, g_bytes)
+    log(f"gdn fwd: {g_ev * 1e3:.1f} us/call back to back, cold median {g_cold['cold_median_us']:.1f} us")
+
+    dec_wall, dec_ev, dec_step = bench_decode(max(args.steps, 10), args.warmup)
     dec_gbs = DN * DH * DEC_BYTES_PER_HEAD / (dec_ev * 1e-3) / 1e9
-    log(f"decode: {dec_ev * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+    dec_cold = cold_stats(dec_step, 10, DN * DH * DEC_BYTES_PER_HEAD)
+    log(f"decode: {dec_ev * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s; cold median "
+        f"{dec_cold['cold_median_us']:.1f} us")
     small = {}
     for n in SMALL_DECODE_N:
-        _, ev = bench_decode(max(args.steps, 20), args.warmup, N=n)
+        _, ev, _ = bench_decode(max(args.steps, 20), args.warmup, N=n)
         _, evg = bench_decode(64, args.warmup, N=n, graph=True)
         small[f"N={n}"] = {"us_per_step": ev * 1e3,
                            "us_per_step_graph": evg * 1e3,
                            "GB_per_s": n * DH * DEC_BYTES_PER_HEAD / (ev * 1e-3) / 1e9}
         log(f"decode N={n}: {ev * 1e3:.1f} us/step, {evg * 1e3:.1f} us/step replayed from a graph")
 
-    lengths, var_wall, var_ev = bench_varlen(args.steps, args.warmup)
+    lengths, var_wall, var_ev, _ = bench_varlen(args.steps, args.warmup)
     var_bytes = VH * VT * FWD_BYTES_PER_TOKEN + len(lengths) * VH * FWD_STATE_BYTES_PER_HEAD
     var_gbs = var_bytes / (var_ev * 1e-3) / 1e9
     log(f"varlen fwd ({len(lengths)} sequences, longest {max(lengths)}): "
@@ -479,11 +573,12 @@ def main():
     log(f"mixer: prologue {mix_pro_ms * 1e3:.1f} us ({mix_pro_gbs:.0f} GB/s), "
         f"epilogue {mix_epi_ms * 1e3:.1f} us ({mix_epi_gbs:.0f} GB/s)")
 
-    bwd_wall, bwd_ev, bwd_ws = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
+    bwd_wall, bwd_ev, bwd_ws, bwd_step = bench_bwd(max(3, args.steps // 4), min(args.warmup, 2))
+    bwd_cold = cold_stats(bwd_step, 5, bwd_bytes)
     bwd_gbs = bwd_bytes / (bwd_ev * 1e-3) / 1e9
     log(f"bwd: {bwd_ev * 1e3:.1f} us/step, {bwd_gbs:.0f} GB/s")
 
-    _, bv_wall, bv_ev = bench_bwd_varlen(max(3, args.steps // 4), min(args.warmup, 2))
+    _, bv_wall, bv_ev, _ = bench_bwd_varlen(max(3, args.steps // 4), min(args.warmup, 2))
     bv_bytes = BH_ * VT * BWD_BYTES_PER_TOKEN + len(lengths) * BH_ * BWD_STATE_BYTES_PER_HEAD
     log(f"bwd varlen: {bv_ev * 1e3:.1f} us/step, {bv_bytes / (bv_ev * 1e-3) / 1e9:.0f} GB/s")
 
@@ -517,6 +612,20 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "event_scope": "HIP events on the launch stream around the timed region's back-to-back "
+                           "calls (mean per call)",
+            **fwd_cold,
+        },
+        "gdn_fwd": {
+            "workload": "gdn_chunk_fwd (Gated DeltaNet: scalar decay, tied scalar beta, S0 = 0) "
+                        "B=4 H=16 T=2048 d_k=d_v=128 chunk=64",
+            "us_per_call": g_ev * 1e3,
+            "head_tokens_per_s": g_ntok / (g_wall * 1e-3),
+            "GB_per_s": g_bytes / (g_ev * 1e-3) / 1e9,
+            "frac_hbm_peak": g_bytes / (g_ev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_call": g_bytes,
+            "bytes_per_head_token": GDN_BYTES_PER_TOKEN + GDN_STATE_BYTES_PER_HEAD / ginp.T,
+            **g_cold,
         },
         "mfma": {
             "achieved": fwd_flops / (ev_ms * 1e-3) / 1e12,
@@ -533,6 +642,7 @@ def main():
             "GB_per_s": dec_gbs,
             "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
             "bytes_per_step": DN * DH * DEC_BYTES_PER_HEAD,
+            **dec_cold,
             "small_batch": {"workload": "decode H=32 d=128, N sequences (latency); us_per_step: "
                                         "back-to-back launches, us_per_step_graph: 64 steps "
                                         "replayed from one HIP graph", **small},
@@ -585,6 +695,7 @@ def main():
             "frac_hbm_peak": bwd_gbs / HBM_PEAK_GBS,
             "bytes_per_step": bwd_bytes,
             "workspace_bytes": bwd_ws,
+            **bwd_cold,
         },
         "varlen_bwd": {
             "workload": (f"gdn2_chunk_bwd_varlen H={BH_}, {VT} tokens per head packed as "

@@ -16,6 +16,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool head_size_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Sequences are counted in 32-bit integers inside the kernels and token
+// offsets in 64-bit ones: B*H must stay below 2^28 and B*H*T below 2^40, so
+// that no product the kernels form can overflow.
+bool sizes_ok(int B, int H, int T) {
+    return (long long)B * H <= (1LL << 28) && (long long)B * H * (long long)T <= (1LL << 40);
+}
+
 // Lazily checks, per device, that the current device is a gfx950.
 gdr_status check_device() {
     int dev = -1;
@@ -59,7 +66,7 @@ const char* gdr_status_string(gdr_status s) {
 size_t gdr_chunk_fwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
                                      uint32_t flags) {
     if (B < 1 || H < 1 || T < 1 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
-    if (T % chunk != 0 || (long long)B * H > (1LL << 28)) return 0;
+    if (T % chunk != 0 || !sizes_ok(B, H, T)) return 0;
     if (!gdr::fwd_wy_supported(d_k, d_v, chunk, flags)) return 0;
     return gdr::fwd_wy_workspace_bytes(B * H, T, d_k, d_v);
 }
@@ -77,7 +84,7 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
-    if ((long long)B * H > (1LL << 28) || (long long)B * H * T > (1LL << 40)) return GDR_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, T)) return GDR_ERR_INVALID_ARG;
     if (!gdr::fwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
     const size_t need = gdr_chunk_fwd_workspace_bytes(B, H, T, d_k, d_v, chunk, flags);
     const bool two_pass = workspace != nullptr && need > 0;
@@ -156,6 +163,7 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const fl
 size_t gdr_chunk_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
                                      uint32_t flags) {
     if (B < 1 || H < 1 || T < 0 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
+    if (T % chunk != 0 || !sizes_ok(B, H, T)) return 0;
     if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return 0;
     return gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
 }
@@ -178,8 +186,9 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
                           dlog_alpha, db, dw, dS0, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDR_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, T)) return GDR_ERR_INVALID_ARG;
     if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return GDR_ERR_UNSUPPORTED;
-    if ((flags & GDR_GATE_LOGITS) && T > 0 && !gdr::fwd_wy_supported(d_k, d_v, chunk, flags))
+    if ((flags & GDR_GATE_LOGITS) && T > 0 && !gdr::bwd_two_pass_supported(d_k, d_v, chunk, flags))
         return GDR_ERR_UNSUPPORTED;
     const size_t need = gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;

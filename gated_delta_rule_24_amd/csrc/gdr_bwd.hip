@@ -42,7 +42,8 @@ namespace gdr {
 
 namespace bwd {
 
-constexpr int VB = 32;                    // value columns per block
+// value columns per block: 32, or all of them for d_v = 16
+template <int DV> constexpr int vb_of() { return DV < 32 ? DV : 32; }
 constexpr float kF16DecayLimit = 10.0f;   // same operand range as the forward kernels
 constexpr float kF32DecayLimit = 80.0f;
 
@@ -346,6 +347,7 @@ __device__ int prep_chunk(const BwdParams& p, size_t tok0, const KeyBufs<F32>& s
 template <int DK, int DV, int C, bool F32>
 struct DstateLayout {
     static constexpr int NT = 256;
+    static constexpr int VB = vb_of<DV>();
     using K = KeyLayout<DK, C, NT, F32>;
     using T = typename Ty<F32>::T;
     static constexpr int TS = K::TS;
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
     using T = typename Ty<F32>::T;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     constexpr int NT = L::NT, NW = NT / 64;
-    constexpr int LDE = K::LDE, LDT = K::LDT, LDV = L::LDV;
+    constexpr int LDE = K::LDE, LDT = K::LDT, LDV = L::LDV, VB = L::VB;
     constexpr int NVB = DV / VB, NB = C / 16, NNT = VB / 16, NMT = DK / 16;
     constexpr int NDT = NMT * NNT, NSW = (NDT + NW - 1) / NW;
 
@@ -482,6 +484,7 @@ __global__ __launch_bounds__(256, 1) void dstate_kernel(BwdParams p) {
 template <int DK, int DV, int C, bool F32>
 struct GradLayout {
     static constexpr int NT = 512;
+    static constexpr int VB = vb_of<DV>();
     using K = KeyLayout<DK, C, NT, F32>;
     using T = typename Ty<F32>::T;
     static constexpr int TS = K::TS;
@@ -489,7 +492,8 @@ struct GradLayout {
     static constexpr int LDW = VB + 4;     // dw block, fp32
     static constexpr int LDG = DK + 4;     // g - g_C, then dg, fp32
     static constexpr int NCT = DK / 16;
-    static constexpr int NPART = NT / DK;  // row parts of the log-decay prefix
+    // row parts of the log-decay prefix (threads tid / DK >= NPART idle there)
+    static constexpr int NPART = (NT / DK < C) ? NT / DK : C;
     // persistent small arrays after the key operands
     static constexpr size_t oPhi = K::oEnd;                          // [DK]
     static constexpr size_t oDWr = oPhi + (size_t)DK * 4;            // [C] dw row sums (scalar w)
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
     using T = typename Ty<F32>::T;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     constexpr int NT = L::NT, NW = NT / 64;
-    constexpr int LDE = K::LDE, LDT = K::LDT, LDV = L::LDV, LDW = L::LDW, LDG = L::LDG;
+    constexpr int LDE = K::LDE, LDT = K::LDT, LDV = L::LDV, LDW = L::LDW, LDG = L::LDG, VB = L::VB;
     constexpr int NVB = DV / VB, NB = C / 16, NNT = VB / 16, NCT = L::NCT;
     constexpr int NKT = NB * NCT, NKS = (NKT + NW - 1) / NW;      // C x DK tiles
     constexpr int NLT = NB * (NB + 1) / 2, NLS = (NLT + NW - 1) / NW;
@@ -786,13 +790,16 @@ __global__ __launch_bounds__(512, 1) void grad_kernel(BwdParams p) {
         // d log alpha_i = Phi - sum_{r<i} dg_r, per channel; NPART threads per channel
         constexpr int NPART = L::NPART, RPP = C / NPART;
         const int ch = tid % DK, part = tid / DK;
+        const bool on = part < NPART;
         float sum = 0.f;
-        for (int r = 0; r < RPP; ++r) sum += sG[(part * RPP + r) * LDG + ch];
-        sTot[part * DK + ch] = sum;
+        if (on) {
+            for (int r = 0; r < RPP; ++r) sum += sG[(part * RPP + r) * LDG + ch];
+            sTot[part * DK + ch] = sum;
+        }
         lds_barrier();
         float off = sPhi[ch];
-        for (int q = 0; q < part; ++q) off -= sTot[q * DK + ch];
-        for (int r = 0; r < RPP; ++r) {
+        for (int q = 0; q < part && on; ++q) off -= sTot[q * DK + ch];
+        for (int r = 0; r < RPP && on; ++r) {
             const int row = part * RPP + r;
             p.dla[(tok0 + row) * DK + ch] = off + poison;
             off -= sG[row * LDG + ch];
@@ -849,7 +856,7 @@ static hipError_t launch_t(const BwdParams& p, hipStream_t st, bool with_dstate)
     if (e != hipSuccess) return e;
     const int NC = p.T / C;
     if (with_dstate) {
-        hipLaunchKernelGGL(kd, dim3((unsigned)(p.BH * (DV / VB))), dim3(LD::NT), LD::bytes, st, p);
+        hipLaunchKernelGGL(kd, dim3((unsigned)(p.BH * (DV / LD::VB))), dim3(LD::NT), LD::bytes, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -857,16 +864,44 @@ static hipError_t launch_t(const BwdParams& p, hipStream_t st, bool with_dstate)
     return hipGetLastError();
 }
 
-// the blocking the backward runs with: fp32 operands need chunks of 32 to fit LDS
+// the blocking the backward runs with: fp32 operands need chunks of at most 32
+// to fit LDS
 int bwd_chunk(int chunk, uint32_t flags) {
-    if (flags & GDR_ACT_F32) return 32;
+    if (flags & GDR_ACT_F32) return chunk < 32 ? chunk : 32;
     return chunk;
 }
 
 }  // namespace bwd
 
+static bool head_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
 bool bwd_supported(int dk, int dv, int chunk, uint32_t /*flags*/) {
-    return dk == dv && (dk == 64 || dk == 128) && (chunk == 32 || chunk == 64);
+    return head_ok(dk) && head_ok(dv) && (chunk == 16 || chunk == 32 || chunk == 64);
+}
+
+// The generic three-launch path for one head shape, blocked with chunks of cb.
+template <int DK, int DV>
+static hipError_t launch_generic(const BwdParams& p, hipStream_t st, int cb, bool f32) {
+    if (f32) {
+        if (cb == 32) return bwd::launch_t<DK, DV, 32, true>(p, st, true);
+        if (cb == 16) return bwd::launch_t<DK, DV, 16, true>(p, st, true);
+        return hipErrorInvalidValue;
+    }
+    if (cb == 64) return bwd::launch_t<DK, DV, 64, false>(p, st, true);
+    if (cb == 32) return bwd::launch_t<DK, DV, 32, false>(p, st, true);
+    if (cb == 16) return bwd::launch_t<DK, DV, 16, false>(p, st, true);
+    return hipErrorInvalidValue;
+}
+
+template <int DK>
+static hipError_t launch_generic_dv(const BwdParams& p, int dv, hipStream_t st, int cb, bool f32) {
+    switch (dv) {
+        case 16: return launch_generic<DK, 16>(p, st, cb, f32);
+        case 32: return launch_generic<DK, 32>(p, st, cb, f32);
+        case 64: return launch_generic<DK, 64>(p, st, cb, f32);
+        case 128: return launch_generic<DK, 128>(p, st, cb, f32);
+    }
+    return hipErrorInvalidValue;
 }
 
 // A second stream per device, at the default priority, for the backward's
@@ -931,8 +966,12 @@ static hipError_t run_two_chains(const BwdParams& p, int dk, int dv, hipStream_t
 
 // the two-pass path keeps S' and the state gradients as f16 fragments, the
 // generic path as fp32 rows
+bool bwd_two_pass_supported(int dk, int dv, int chunk, uint32_t flags) {
+    return dk == dv && fwd_wy_supported(dk, dv, bwd::bwd_chunk(chunk, flags), flags);
+}
+
 static bool bwd_two_pass(int dk, int dv, int T, int cb, uint32_t flags) {
-    return T > 0 && fwd_wy_supported(dk, dv, cb, flags);
+    return T > 0 && dk == dv && fwd_wy_supported(dk, dv, cb, flags);
 }
 
 size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags) {
@@ -987,13 +1026,13 @@ hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t
     if (used != cb) return hipErrorInvalidValue;
     // 2 and 3
     const bool f32 = (p.flags & GDR_ACT_F32) != 0;
-    const bool ds = true;
-    if (dk == 128) {
-        if (f32) return bwd::launch_t<128, 128, 32, true>(p, st, ds);
-        return cb == 64 ? bwd::launch_t<128, 128, 64, false>(p, st, ds) : bwd::launch_t<128, 128, 32, false>(p, st, ds);
+    switch (dk) {
+        case 16: return launch_generic_dv<16>(p, dv, st, cb, f32);
+        case 32: return launch_generic_dv<32>(p, dv, st, cb, f32);
+        case 64: return launch_generic_dv<64>(p, dv, st, cb, f32);
+        case 128: return launch_generic_dv<128>(p, dv, st, cb, f32);
     }
-    if (f32) return bwd::launch_t<64, 64, 32, true>(p, st, ds);
-    return cb == 64 ? bwd::launch_t<64, 64, 64, false>(p, st, ds) : bwd::launch_t<64, 64, 32, false>(p, st, ds);
+    return hipErrorInvalidValue;
 }
 
 // Packed sequences: the same three steps over the packed records, S' and D

@@ -523,12 +523,22 @@ static hipError_t launch_d(const FwdParams& p, int chunk, hipStream_t st, int* u
     return launch_c<DK, DV, false>(p, chunk, st, used);
 }
 
+static bool head_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
 bool fwd_supported(int dk, int dv, int chunk, uint32_t flags) {
     (void)flags;
-    if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
-    if (dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128)) return true;
-    if ((dk == 64 && dv == 128) || (dk == 128 && dv == 64)) return true;
-    return false;
+    return (chunk == 16 || chunk == 32 || chunk == 64) && head_ok(dk) && head_ok(dv);
+}
+
+template <int DK>
+static hipError_t launch_dv(const FwdParams& p, int dv, int chunk, hipStream_t st, int* used) {
+    switch (dv) {
+        case 16: return launch_d<DK, 16>(p, chunk, st, used);
+        case 32: return launch_d<DK, 32>(p, chunk, st, used);
+        case 64: return launch_d<DK, 64>(p, chunk, st, used);
+        case 128: return launch_d<DK, 128>(p, chunk, st, used);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dk, int dv, int chunk, hipStream_t st, int* used) {
@@ -536,12 +546,12 @@ hipError_t launch_fwd(const FwdParams& p, int dk, int dv, int chunk, hipStream_t
         if (used) *used = chunk;
         return launch_fwd_pipe(p, dk, dv, st);
     }
-    if (dk == 16 && dv == 16) return launch_d<16, 16>(p, chunk, st, used);
-    if (dk == 32 && dv == 32) return launch_d<32, 32>(p, chunk, st, used);
-    if (dk == 64 && dv == 64) return launch_d<64, 64>(p, chunk, st, used);
-    if (dk == 128 && dv == 128) return launch_d<128, 128>(p, chunk, st, used);
-    if (dk == 64 && dv == 128) return launch_d<64, 128>(p, chunk, st, used);
-    if (dk == 128 && dv == 64) return launch_d<128, 64>(p, chunk, st, used);
+    switch (dk) {
+        case 16: return launch_dv<16>(p, dv, chunk, st, used);
+        case 32: return launch_dv<32>(p, dv, chunk, st, used);
+        case 64: return launch_dv<64>(p, dv, chunk, st, used);
+        case 128: return launch_dv<128>(p, dv, chunk, st, used);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -376,9 +376,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW), 1) void fwd_pipe_kernel(FwdParams
             }
             lds_barrier();
         }
-        // never true (flag bit 31 is rejected by the API); keeps the touch loads
+        // a register sink that keeps the touch loads (no store)
         touch ^= tpend[0] ^ tpend[1];
-        if ((p.flags & 0x80000000u) && touch == 0x12345u) p.Sf[0] = 0.f;
+        asm volatile("" ::"v"(touch));
     } else {
         // ======================================================== consumer
         const int cw = wave;

@@ -752,8 +752,8 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
             }
 #pragma unroll
             for (int r = 0; r < LPL; ++r) tacc ^= ta[r] ^ tb[r];
-            // never true (flag bit 31 is rejected by the API); keeps the touch loads
-            if ((p.flags & 0x80000000u) && tacc == 0x12345u) p.Sf[0] = 0.f;
+            // a register sink that keeps the touch loads (no store)
+            asm volatile("" ::"v"(tacc));
             return;
         }
         if (NC > 0) {
@@ -821,8 +821,8 @@ __global__ __launch_bounds__(128, 1) void chain_kernel(FwdParams p, const unsign
         }
 #pragma unroll
         for (int r = 0; r < LPL; ++r) tacc ^= ta[r] ^ tb[r];
-        // never true (flag bit 31 is rejected by the API); keeps the touch loads
-        if ((p.flags & 0x80000000u) && tacc == 0x12345u) p.Sf[0] = 0.f;
+        // a register sink that keeps the touch loads (no store)
+        asm volatile("" ::"v"(tacc));
         return;
     }
 

@@ -144,6 +144,9 @@ hipError_t launch_bwd_wgrad(const BwdParams& p, int dk, int dv, const void* reco
 // split of that workspace: states, then state gradients, then the forward records
 size_t bwd_states_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
 bool bwd_supported(int dk, int dv, int chunk, uint32_t flags);
+// the two-pass backward (WY records, reverse chain, per-chunk gradients):
+// bf16, chunk 64, d_k = d_v in {64, 128}; the only one taking GDR_GATE_LOGITS
+bool bwd_two_pass_supported(int dk, int dv, int chunk, uint32_t flags);
 hipError_t launch_bwd(const BwdParams& p, int dk, int dv, int chunk, hipStream_t st);
 // Packed sequences (bf16, d_k == d_v in {64, 128}): workspace = records, S'
 // fragments, D fragments (each for packed_max_chunks per head), prep arrays.

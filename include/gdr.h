@@ -213,8 +213,11 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
  * it before the call's last kernel (event fork and join), so every effect is
  * ordered on `stream` as if it ran there, also under graph capture.  Calls on
  * one device share that second stream.
- * Supported: bf16 or fp32 activations, d_k = d_v = 128 or 64, chunk 64 or
- * 32.  Returns GDR_ERR_UNSUPPORTED otherwise.
+ * Supported: bf16 or fp32 activations, d_k and d_v each in {16, 32, 64,
+ * 128}, chunk 16, 32 or 64 (fp32 activations block with at most 32; results
+ * do not depend on the blocking beyond rounding).  Returns
+ * GDR_ERR_UNSUPPORTED otherwise.  GDR_GATE_LOGITS needs bf16 activations,
+ * chunk 64 and d_k = d_v in {64, 128}.
  */
 size_t gdr_chunk_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v,
                                      int chunk, uint32_t flags);

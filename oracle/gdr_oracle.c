@@ -48,8 +48,7 @@
 #endif
 
 /* One token step on a single head.  S is dk x dv, updated in place.
- * If S_prev_decayed != NULL the decayed state D_t S_{t-1} is stored there
- * (needed by the reverse mode).  o receives S_t^T q_t (dv values). */
+ * o receives S_t^T q_t (dv values); r is scratch for the erase read. */
 static void token_step(int dk, int dv, double* S, const double* q,
                        const double* k, const double* v, const double* la,
                        const double* b, const double* w, double* o,

@@ -20,8 +20,9 @@ taken is:
 - L2norm(x) = x / sqrt(sum x^2 + 1e-6) over a head's channels;
 - RMS norm: x / sqrt(mean x^2 + 1e-6) times a per-channel weight shared by
   the heads;
-- the decay gate is a sigmoid like the others (the Q&A page writes alpha as
-  a sigmoid of a projection), so log alpha = log(sigmoid(a_pre)).
+- the decay gate is a sigmoid like the others (the "Gated DeltaNet"
+  explainer, data-dependent gating section, writes alpha as a sigmoid of a
+  projection of the input), so log alpha = log(sigmoid(a_pre)).
 
 The definitions are written once, as plain float64 torch operations on the
 CPU (numpy arrays in and out).  The backward functions differentiate exactly

@@ -65,7 +65,7 @@ def _fwd(lib, **kw):
     (dict(q=None), 1), (dict(o=None), 1), (dict(w=None), 1),
     (dict(chunk=48), 1), (dict(T=100), 1), (dict(B=0), 1), (dict(T=-64), 1),
     (dict(flags=0x100), 1), (dict(k=MIS), 1), (dict(Sf=MIS), 1),
-    (dict(dk=96), 2), (dict(dv=256), 2), (dict(dk=16, dv=128), 2),
+    (dict(dk=96), 2), (dict(dv=256), 2), (dict(dk=16, dv=96), 2),
 ])
 def test_fwd_argument_validation(kw, status):
     assert _fwd(_lib(), **kw) == status
@@ -115,8 +115,13 @@ def test_bwd_workspace_query_and_validation():
     # fp32 activations block the backward with chunks of 32
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 64, 1) == 2 * 2 * 4 * 64 * 64 * 4
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 48, 0) == 0
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 32, 32, 64, 0) == 0
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 64, 64, 0) == 0
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 96, 64, 0) == 0
+    # other head shapes and chunks run the generic path: fp32 chunk-start states
+    # and chunk-end gradients (2 x B*H x T/chunk x d_k x d_v x 4 bytes)
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 32, 32, 64, 0) == 2 * 2 * 2 * 32 * 32 * 4
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 64, 64, 0) == 2 * 2 * 2 * 128 * 64 * 4
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 16, 128, 16, 0) == 2 * 2 * 8 * 16 * 128 * 4
+    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 16, 1) == 2 * 2 * 8 * 64 * 64 * 4
 
     def call(ws=A, nbytes=1 << 30, **kw):
         a = dict(B=1, H=2, T=128, dk=128, dv=128, chunk=64, flags=0)
@@ -128,8 +133,8 @@ def test_bwd_workspace_query_and_validation():
     assert call(T=100) == 1
     assert call(flags=0x2) == 1          # bf16 output has no meaning for gradients
     assert call(ws=MIS) == 1
-    assert call(dk=32, dv=32) == 2
-    assert call(chunk=16) == 2
+    assert call(dk=96, dv=32) == 2
+    assert call(chunk=48) == 1
 
 
 def _fwd_varlen(lib, **kw):
@@ -263,3 +268,23 @@ def test_mixer_backward_validation():
     assert lib.gdr_mixer_prologue_bwd(*([A] * 14 + [None]), 2, 3, 200, 128, 128, 0, A, nb, None) == 1
     assert lib.gdr_mixer_epilogue_bwd(*([A] * 7), 1, 1, 8, 64, 0, A, 1024 * 64 * 4 - 1, None) == 3
     assert lib.gdr_mixer_epilogue_bwd(*([A] * 7), 1, 1, 8, 96, 0, A, 1 << 20, None) == 2
+
+
+def test_size_overflow_is_rejected_before_any_launch():
+    """B*H above 2^28 or B*H*T above 2^40 would overflow the kernels' sequence
+    and token arithmetic: the forward, the backward and their workspace
+    queries refuse such sizes (status / 0 bytes) instead of launching."""
+    lib = _lib()
+    big = dict(B=1 << 15, H=1 << 14)                   # B*H = 2^29
+    assert _fwd(lib, **big) == 1
+    assert _fwd(lib, B=1 << 12, H=1 << 12, T=1 << 17) == 1   # B*H*T = 2^41
+    assert lib.gdr_chunk_fwd_workspace_bytes(1 << 15, 1 << 14, 64, 128, 128, 64, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace_bytes(1 << 12, 1 << 12, 1 << 17, 128, 128, 64, 0) == 0
+    assert lib.gdr_chunk_bwd_workspace_bytes(1 << 15, 1 << 14, 64, 128, 128, 64, 0) == 0
+    assert lib.gdr_chunk_bwd_workspace_bytes(1 << 12, 1 << 12, 1 << 17, 128, 128, 64, 0) == 0
+
+    def bwd(B, H, T):
+        return lib.gdr_chunk_bwd(A, A, A, A, A, A, A, A, None, A, A, A, A, A, A, A, B, H, T, 128, 128,
+                                 64, 0, A, 1 << 62, None)
+    assert bwd(1 << 15, 1 << 14, 64) == 1
+    assert bwd(1 << 12, 1 << 12, 1 << 17) == 1

@@ -103,6 +103,24 @@ CASES = [
     ("f32_scalar_gdn", dict(B=1, H=2, T=96, dk=64, dv=64, act="f32", chunk=32, alpha_mode="scalar",
                             b_mode="scalar", w_mode="scalar", tied=True), 1e-4, True),
     ("f32_strong_decay", dict(B=1, H=1, T=128, dk=64, dv=64, act="f32", decay_scale=0.5), 1e-4, True),
+    # every head size, d_k != d_v and chunks of 16 (the generic kernels)
+    ("bf16_d16_c16", dict(B=1, H=2, T=80, dk=16, dv=16, chunk=16), 2e-2, True),
+    ("bf16_d32_c64", dict(B=2, H=1, T=192, dk=32, dv=32), 2e-2, False),
+    ("bf16_d32_c16", dict(B=1, H=2, T=96, dk=32, dv=32, chunk=16), 2e-2, True),
+    ("bf16_d16x128_c32", dict(B=1, H=2, T=96, dk=16, dv=128, chunk=32), 2e-2, True),
+    ("bf16_d128x16_c64", dict(B=1, H=2, T=192, dk=128, dv=16), 2e-2, True),
+    ("bf16_d64x32_c16", dict(B=1, H=2, T=64, dk=64, dv=32, chunk=16), 2e-2, False),
+    ("bf16_d32x64_c64", dict(B=1, H=1, T=128, dk=32, dv=64, alpha_mode="scalar"), 2e-2, True),
+    ("bf16_d128x64_c64", dict(B=1, H=2, T=128, dk=128, dv=64), 2e-2, True),
+    ("bf16_d64x128_c32", dict(B=1, H=2, T=128, dk=64, dv=128, chunk=32, b_mode="scalar"), 2e-2, False),
+    ("bf16_d128_c16", dict(B=1, H=1, T=96, dk=128, dv=128, chunk=16), 2e-2, True),
+    ("f32_d16_c16", dict(B=1, H=2, T=64, dk=16, dv=16, act="f32", chunk=16), 1e-4, True),
+    ("f32_d32x128_c32", dict(B=1, H=2, T=64, dk=32, dv=128, act="f32", chunk=32), 1e-4, False),
+    ("f32_d128x32_c16", dict(B=1, H=1, T=64, dk=128, dv=32, act="f32", chunk=16,
+                             w_mode="scalar"), 1e-4, True),
+    ("f32_gdn_tiny_c16", dict(B=1, H=1, T=64, dk=16, dv=16, act="f32", chunk=16, alpha_mode="scalar",
+                              b_mode="scalar", w_mode="scalar", tied=True, alpha_dist="uniform",
+                              s0_std=None), 1e-4, False),
 ]
 
 
