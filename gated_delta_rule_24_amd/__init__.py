@@ -66,6 +66,8 @@ def _load():
         lib.gdr_chunk_fwd_workspace_bytes.restype = S
         lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 6 + [U, P, S, P]
         lib.gdr_chunk_fwd.restype = I
+        lib.gdr_chunk_fwd_noalloc.argtypes = [P] * 9 + [I] * 6 + [U, P]
+        lib.gdr_chunk_fwd_noalloc.restype = I
         lib.gdr_chunk_fwd_varlen_workspace_bytes.argtypes = [I] * 5 + [U]
         lib.gdr_chunk_fwd_varlen_workspace_bytes.restype = S
         lib.gdr_chunk_fwd_varlen.argtypes = [P] * 10 + [I] * 5 + [U, P, S, P]
@@ -100,7 +102,7 @@ def lib():
 
 
 EXPORTED_SYMBOLS = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
-                    "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
+                    "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_varlen_workspace_bytes", "gdr_chunk_fwd_varlen",
                     "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
                     "gdr_chunk_bwd_varlen_workspace_bytes", "gdr_chunk_bwd_varlen",
                     "gdr_mixer_prologue", "gdr_mixer_epilogue", "gdr_mixer_bwd_workspace_bytes",
@@ -163,6 +165,18 @@ def gdr_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, B, H, T, d_k, d_v, c
                                _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, d_k, d_v, chunk,
                                flags, _ptr(workspace), workspace_bytes, _stream(stream))
     _check("gdr_chunk_fwd", st)
+
+
+# bytes of the library-owned device array gdr_chunk_fwd_noalloc uses per GPU
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, log_alpha, b, w, S0, o, S_final, B, H, T, d_k, d_v, chunk,
+                          flags, stream=None):
+    st = _load().gdr_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                       _ptr(w), _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, d_k, d_v,
+                                       chunk, flags, _stream(stream))
+    _check("gdr_chunk_fwd_noalloc", st)
 
 
 def gdr_chunk_fwd_varlen_workspace_bytes(nseq, H, T, d_k, d_v, flags) -> int:

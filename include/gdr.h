@@ -134,6 +134,31 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * gdr_chunk_fwd without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * results are those of gdr_chunk_fwd.  Where gdr_chunk_fwd would take a
+ * workspace, this call uses a library-owned device array of
+ * GDR_NOALLOC_SCRATCH_BYTES on the current GPU instead (each GPU the library
+ * runs on holds its own copy until the process ends; it is looked up once per
+ * device at the first call there).  A call whose
+ * gdr_chunk_fwd_workspace_bytes() exceeds GDR_NOALLOC_SCRATCH_BYTES returns
+ * GDR_ERR_WORKSPACE and launches nothing (at d_k = d_v = 128 the array holds
+ * the operands of 900 chunks of 64 tokens, e.g. B*H = 16 heads of T = 3584).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or different host threads) race and must be
+ * ordered by the caller.  The array's contents between calls are never read
+ * before being written.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdr_status gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const void* b, const void* w,
+                                 const float* S0, void* o, float* S_final,
+                                 int B, int H, int T, int d_k, int d_v, int chunk,
+                                 uint32_t flags, void* stream);
+
+/*
  * The same forward over packed variable-length sequences: nseq sequences of
  * any lengths stored back to back (variable-length batches are the practical
  * extension the pages point to: "Gated DeltaNet study notes" §4-3).  Each
