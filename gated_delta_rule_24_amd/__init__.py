@@ -37,6 +37,7 @@ GDR_B_SCALAR = 0x8
 GDR_W_SCALAR = 0x10
 GDR_FWD_GENERIC = 0x20
 GDR_GATE_LOGITS = 0x40
+GDR_FWD_SPLIT = 0x80
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "launch", 5: "device"}
 
@@ -276,8 +277,10 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
               generic: bool = False, path: str = "auto", gate_logits: bool = False):
     """q, k: [B,H,T,dk]; v: [B,H,T,dv]; log_alpha, b: [B,H,T,dk] or [B,H,T];
     w: [B,H,T,dv] or [B,H,T]; S0: [B,H,dk,dv] fp32 or None.
-    path "auto" passes a workspace (two-pass kernels where they apply),
-    "fused" passes none (single-kernel path).
+    path "auto" passes a workspace (the chunk producer and the state chains in
+    one persistent kernel where they apply), "split" the same with the two
+    roles as two kernels one after the other (GDR_FWD_SPLIT), "fused" passes
+    no workspace (single-kernel path).
     Returns (o [B,H,T,dv], S_final [B,H,dk,dv] or None)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -289,7 +292,9 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, chunk: int = 64,
     o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
     Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
     ws, nbytes = None, 0
-    if path == "auto":
+    if path == "split":
+        flags |= GDR_FWD_SPLIT
+    if path in ("auto", "split"):
         nbytes = gdr_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, flags)
         if nbytes > 0:
             ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -10,7 +10,7 @@
 namespace {
 
 constexpr uint32_t kKnownFlags = GDR_ACT_F32 | GDR_OUT_BF16 | GDR_ALPHA_SCALAR | GDR_B_SCALAR |
-                                 GDR_W_SCALAR | GDR_FWD_GENERIC | GDR_GATE_LOGITS;
+                                 GDR_W_SCALAR | GDR_FWD_GENERIC | GDR_GATE_LOGITS | GDR_FWD_SPLIT;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -68,7 +68,7 @@ size_t gdr_chunk_fwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int 
     if (B < 1 || H < 1 || T < 1 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
     if (T % chunk != 0 || !sizes_ok(B, H, T)) return 0;
     if (!gdr::fwd_wy_supported(d_k, d_v, chunk, flags)) return 0;
-    return gdr::fwd_wy_workspace_bytes(B * H, T, d_k, d_v);
+    return gdr::fwd_fz_workspace_bytes(B * H, T, d_k, d_v);
 }
 
 gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -98,7 +98,7 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
     p.cu_seqlens = nullptr; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = 0;
     p.BH = B * H; p.T = T; p.flags = flags;
-    if (two_pass) return from_hip(gdr::launch_fwd_wy(p, d_k, d_v, workspace, (hipStream_t)stream));
+    if (two_pass) return from_hip(gdr::launch_fwd_fz(p, d_k, d_v, workspace, (hipStream_t)stream));
     int used = 0;
     return from_hip(gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used));
 }
@@ -143,7 +143,7 @@ gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
 gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                            const void* b, const void* w, float* S, void* o, int N, int H,
                            int d_k, int d_v, uint32_t flags, void* stream) {
-    if (flags & ~kKnownFlags) return GDR_ERR_INVALID_ARG;
+    if (flags & ~(kKnownFlags & ~GDR_FWD_SPLIT)) return GDR_ERR_INVALID_ARG;
     if (N < 1 || H < 1) return GDR_ERR_INVALID_ARG;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDR_ERR_UNSUPPORTED;
     if (!q || !k || !v || !log_alpha || !b || !w || !S || !o) return GDR_ERR_INVALID_ARG;

@@ -87,6 +87,11 @@ size_t fwd_wy_workspace_bytes(int BH, int T, int dk, int dv, bool bwd_layouts = 
 constexpr int kWyPass = 1, kChainPass = 2;
 hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st,
                          bool bwd_layouts = false, int passes = kWyPass | kChainPass);
+// The forward's producer / state-chain path (gdr_fwd_fz.hip): bf16
+// activations, chunk 64, d_k and d_v in {64, 128}, T > 0 (the shapes of
+// fwd_wy_supported without the backward layouts).
+size_t fwd_fz_workspace_bytes(int BH, int T, int dk, int dv);
+hipError_t launch_fwd_fz(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st);
 // Packed variable-length sequences.  Each head holds at most T/64 + nseq
 // chunks; records and fragments are numbered head * (chunk count) + chunk.
 // The prep step fills, in prep_bytes of device memory: the chunk offsets of

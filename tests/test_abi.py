@@ -74,8 +74,13 @@ def test_fwd_argument_validation(kw, status):
 def test_fwd_workspace_query_and_validation():
     lib = _lib()
     one = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0)
-    assert one > 3 * 64 * 128 * 2          # at least W, Q and Kh of one chunk in f16
-    assert lib.gdr_chunk_fwd_workspace_bytes(2, 3, 256, 128, 128, 64, 0) == 2 * 3 * 4 * one
+    # per chunk of 64 tokens a record (W, Kh^T, U', Q_s as 64 x 128 f16, P as
+    # 64 x 64 f16, 1 KiB of decay), then one int32 flag per chunk (padded to 64)
+    # and 64 int32 control words
+    rec = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 1024
+    assert one == rec + (64 + 64) * 4
+    assert lib.gdr_chunk_fwd_workspace_bytes(2, 3, 256, 128, 128, 64, 0) == 2 * 3 * 4 * rec + (64 + 64) * 4
+    assert lib.gdr_chunk_fwd_workspace_bytes(1, 40, 6400, 128, 128, 64, 0) == 4000 * rec + (4032 + 64) * 4
     assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0x1) == 0   # fp32: fused only
     assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 32, 0) == 0
     assert lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 32, 32, 64, 0) == 0
@@ -97,7 +102,8 @@ def test_decode_argument_validation():
     assert call(S=None) == 1
     assert call(N=0) == 1
     assert call(o=MIS) == 1
-    assert call(flags=0x80) == 1
+    assert call(flags=0x100) == 1
+    assert call(flags=0x80) == 1         # a forward-only flag
     assert call(dk=48) == 2
 
 
@@ -108,8 +114,8 @@ def test_bwd_workspace_query_and_validation():
     # extended by three 64 x d_k and two 64 x 64 f16 operand layouts for the
     # backward passes
     states = 2 * 2 * 2 * 128 * 128 * 2
-    records = lib.gdr_chunk_fwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0)
-    assert records > 0
+    # the backward's own records: W, Kh^T, U', Q', P (f16) and the decay slot
+    records = 2 * 2 * (4 * 64 * 128 * 2 + 64 * 64 * 2 + 768)
     extra = 2 * 2 * (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2)
     assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0) == states + records + extra
     # fp32 activations block the backward with chunks of 32
@@ -164,10 +170,12 @@ def test_fwd_varlen_workspace_query():
     # so H * (T//64 + nseq) records cover any split of T tokens into nseq sequences;
     # then the nseq+1 chunk offsets, the (T//64 + nseq) x 2 chunk table and the
     # nseq-long sequence order (int32), each rounded up to 256 bytes
-    rec = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0)
+    # the packed records: W, Kh^T, U', Q', P as f16 (d x 64 each, P 64 x 64) and
+    # the decay slot (4 d + 16 bytes rounded up to 256)
+    rec = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 768
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(3, 2, 200, 128, 128, 0) == 2 * (3 + 3) * rec + 768
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(64, 1, 0, 128, 128, 0) == 64 * rec + 1280
-    rec64 = lib.gdr_chunk_fwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0)
+    rec64 = 4 * 64 * 64 * 2 + 64 * 64 * 2 + 512
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 4, 128, 64, 64, 0x1c) == 4 * 3 * rec64 + 768
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0   # fp32
