@@ -35,8 +35,9 @@
 //
 // The producer writes each chunk's record (W, Kh^T, U', Q_s, P as MFMA
 // fragments, then e^{g_C}) to the workspace; the chain keeps the state in
-// MFMA accumulators and copies each chunk's record into LDS once per
-// workgroup with direct global-to-LDS loads.
+// MFMA accumulators, one workgroup per 64 value columns of a head, and copies
+// each chunk's record into LDS once per workgroup with direct global-to-LDS
+// loads.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 #include "gdr_wy.h"
@@ -741,17 +742,21 @@ struct Producer {
 // ---------------------------------------------------------------------------
 // state chain
 // ---------------------------------------------------------------------------
-// One workgroup of four waves per chain (one head's sequence); wave w owns
-// the DV/4 value columns w*DV/4 .., as DV/64 strips of 16 columns with their
-// fp32 state in MFMA accumulators.  Each chunk's record is copied into LDS
-// once per workgroup (direct global-to-LDS loads, one chunk ahead, two
-// stages), so the shared operands cross the L2 once per head and chunk; every
-// wave reads its fragments from LDS, and each W, Q_s, P and Kh^T fragment
-// feeds all the wave's strips.
+// A head's DV value columns are split into DV/64 blocks of 64, and each block
+// is one workgroup of four waves; wave w of a block owns its 16 columns
+// 16 w .. 16 w + 15, with their fp32 state in MFMA accumulators.  Each chunk's
+// record is copied into LDS once per workgroup (direct global-to-LDS loads,
+// one chunk ahead, two stages); every wave reads its fragments from LDS.
+// (Wider blocks, one workgroup per head, measured slower: the four waves of a
+// workgroup read the same W, Kh^T, Q_s and P fragments, so the LDS traffic per
+// chunk does not shrink with the block, while the arithmetic per wave grows.)
+constexpr int kChainCols = 64;
+
 template <int DK, int DV>
 struct ChainLayout {
     using R = RecF<DK, DV>;
-    static constexpr int SPW = DV / 64;                      // strips per wave
+    static constexpr int SPW = kChainCols / 64;              // strips per wave
+    static constexpr int WPH = DV / kChainCols;              // workgroups per head
     static constexpr size_t stage = R::bytes;                // one whole record
     static constexpr size_t oOk = 2 * stage;                 // int[2]: a record is ready
     static constexpr size_t bytes = oOk + 16;
@@ -808,8 +813,8 @@ struct Chain {
     // first barrier and the flag's latency hides behind the arithmetic.
     template <typename Ready>
     __device__ __forceinline__ void run(const FwdParams& p, const unsigned char* rec0, size_t RB, int NC, int bh,
-                                        size_t tok_base, Ready& rd) {
-        const int col0 = 16 * SPW * wave;                    // this wave's first column
+                                        size_t tok_base, int colbase, Ready& rd) {
+        const int col0 = colbase + 16 * SPW * wave;          // this wave's first column
         int* s_ok = reinterpret_cast<int*>(smem + L::oOk);   // [2]: chunk x's readiness in slot x & 1
         floatx4 S[SPW][NKT];
 #pragma unroll
@@ -886,7 +891,7 @@ struct Chain {
 #pragma unroll
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
-                for (int kk = 0; kk < NK2; ++kk) uq[s][kk] = frag(R::U + (size_t)((SPW * wave + s) * NK2 + kk) * 1024);
+                for (int kk = 0; kk < NK2; ++kk) uq[s][kk] = frag(R::U + (size_t)((col0 / 16 + s) * NK2 + kk) * 1024);
 #pragma unroll
             for (int mt = 0; mt < NKT; ++mt) gm[mt] = *reinterpret_cast<const floatx4*>(G + 16 * mt + g4);
             floatx4 Y[SPW][NB];
@@ -1046,7 +1051,8 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(FwdParams p, const unsign
     using CH = Chain<DK, DV>;
     using R = RecF<DK, DV>;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int bh = blockIdx.x;
+    constexpr int WPH = CH::L::WPH;
+    const int bh = blockIdx.x / WPH;
     const int NC = p.T / C;
     CH ch;
     ch.init(smem);
@@ -1054,7 +1060,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(FwdParams p, const unsign
         __device__ void poll(int) {}
         __device__ bool wait(int) { return true; }
     } rd;
-    ch.run(p, ws + (size_t)bh * NC * R::bytes, R::bytes, NC, bh, (size_t)bh * p.T, rd);
+    ch.run(p, ws + (size_t)bh * NC * R::bytes, R::bytes, NC, bh, (size_t)bh * p.T, (blockIdx.x % WPH) * kChainCols, rd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1063,10 +1069,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(FwdParams p, const unsign
 // The grid is one workgroup per compute unit.  Each workgroup reads the id of
 // the XCD it runs on and takes a rank among that XCD's workgroups.  Heads are
 // dealt to the XCDs (head h to XCD slot h mod NX); on each XCD the first
-// workgroups (at most CAP) run the chains of its heads, the others produce
-// that XCD's chunks, claimed one at a time from a per-XCD counter, in the
-// order the chains consume them (chunk-major within each batch of chained
-// heads).  A record is written to the XCD's L2 and read from there: producer
+// workgroups (at most CAP, a whole number of heads' column blocks) run the
+// chains of its heads, the others produce that XCD's chunks, claimed one at a
+// time from a per-XCD counter, in the order the chains consume them
+// (chunk-major within each batch of heads chained at once).  A record is written to the XCD's L2 and read from there: producer
 // and consumer share the L2, which orders their accesses.  A producer
 // publishes a chunk (a flag, written after every wave has seen its record
 // stores complete) while it works on its next chunk; a chain waits for the
@@ -1077,7 +1083,7 @@ struct FusedCfg {
     int* flags;        // [BH * NC] chunk published
     int* ctl;          // [64]
     int NX;            // XCD slots
-    int CAP;           // chain workgroups per slot at most
+    int CAP;           // chain workgroups per slot at most (at least one head's blocks)
     unsigned spin;     // polls before a chain gives up
 };
 
@@ -1107,12 +1113,14 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(FwdParams p, unsigned cha
     }
     __syncthreads();
     const int slot = s_role[0], rank = s_role[1];
+    constexpr int WPH = CH::L::WPH;                                          // column blocks per head
     const int nh = slot < p.BH ? (p.BH - slot + cfg.NX - 1) / cfg.NX : 0;   // heads of this slot
-    const int nch = nh < cfg.CAP ? nh : cfg.CAP;                             // chains at once
-    if (rank < nch) {
+    const int cap = cfg.CAP / WPH > 0 ? cfg.CAP / WPH : 1;
+    const int nch = nh < cap ? nh : cap;                                     // heads chained at once
+    if (rank < nch * WPH) {
         CH ch;
         ch.init(smem);
-        for (int j = rank; j < nh; j += nch) {
+        for (int j = rank / WPH; j < nh; j += nch) {
             const int h = slot + cfg.NX * j;
             // the flags of this head's chunks; poll() issues the load, wait()
             // uses it and spins (bounded) while the flag is still clear
@@ -1136,7 +1144,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(FwdParams p, unsigned cha
             rd.fl = cfg.flags + (size_t)h * NC;
             rd.spin = cfg.spin;
             rd.seen = 0;
-            ch.run(p, ws + (size_t)h * NC * R::bytes, R::bytes, NC, h, (size_t)h * p.T, rd);
+            ch.run(p, ws + (size_t)h * NC * R::bytes, R::bytes, NC, h, (size_t)h * p.T, (rank % WPH) * kChainCols, rd);
         }
         return;
     }
@@ -1305,7 +1313,8 @@ static hipError_t launch_split_t(const FwdParams& p, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(kp, dim3((unsigned)gp), dim3(PL::NT), PL::bytes, st, p, reinterpret_cast<unsigned char*>(ws));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kc, dim3((unsigned)p.BH), dim3(256), CL::bytes, st, p, reinterpret_cast<const unsigned char*>(ws));
+    hipLaunchKernelGGL(kc, dim3((unsigned)(p.BH * CL::WPH)), dim3(256), CL::bytes, st, p,
+                       reinterpret_cast<const unsigned char*>(ws));
     return hipGetLastError();
 }
 
