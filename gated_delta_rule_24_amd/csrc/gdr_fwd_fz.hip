@@ -743,19 +743,21 @@ struct Producer {
 // state chain
 // ---------------------------------------------------------------------------
 // A head's DV value columns are split into DV/64 blocks of 64, and each block
-// is one workgroup of four waves; wave w of a block owns its 16 columns
-// 16 w .. 16 w + 15, with their fp32 state in MFMA accumulators.  Each chunk's
-// record is copied into LDS once per workgroup (direct global-to-LDS loads,
-// one chunk ahead, two stages); every wave reads its fragments from LDS.
-// (Wider blocks, one workgroup per head, measured slower: the four waves of a
-// workgroup read the same W, Kh^T, Q_s and P fragments, so the LDS traffic per
-// chunk does not shrink with the block, while the arithmetic per wave grows.)
+// is one workgroup of four waves: two compute waves, each owning 32 of the
+// block's columns (their fp32 state in MFMA accumulators), and two copy waves
+// that move each chunk's record into LDS (direct global-to-LDS loads, one
+// chunk ahead, two stages) and watch the records' readiness.  The compute
+// waves read every fragment from LDS and touch global memory only to store
+// the output.  Every compute wave reads the chunk's full W, Kh^T, Q_s and P,
+// so LDS traffic grows with the number of compute waves: two waves per 64
+// columns measured faster than four waves per 64 or per 128 columns.
 constexpr int kChainCols = 64;
+constexpr int kComputeWaves = 2;
 
 template <int DK, int DV>
 struct ChainLayout {
     using R = RecF<DK, DV>;
-    static constexpr int SPW = kChainCols / 64;              // strips per wave
+    static constexpr int SPW = kChainCols / (16 * kComputeWaves);   // strips per compute wave
     static constexpr int WPH = DV / kChainCols;              // workgroups per head
     static constexpr size_t stage = R::bytes;                // one whole record
     static constexpr size_t oOk = 2 * stage;                 // int[2]: a record is ready
@@ -796,38 +798,31 @@ struct Chain {
         g4 = 4 * (lane >> 4);
     }
 
-    // this wave's share of the copies of chunk record `rec` into stage st
+    // a copy wave's share of the copies of chunk record `rec` into stage st
     __device__ __forceinline__ void fetch(const unsigned char* rec, int st) {
         unsigned char* dst = smem + (size_t)st * L::stage;
-        for (int i = wave; i < L::NLOAD; i += 4) copy_1k(rec + (size_t)i * 1024, dst + (size_t)i * 1024, lane);
+        for (int i = wave - kComputeWaves; i < L::NLOAD; i += 4 - kComputeWaves)
+            copy_1k(rec + (size_t)i * 1024, dst + (size_t)i * 1024, lane);
     }
 
     // The chain of sequence bh over NC chunks whose records start at rec0 (RB
-    // bytes apart).  A record's readiness is asked by wave 0 only, through rd:
+    // bytes apart).  A record's readiness is asked by the first copy wave only,
+    // through rd:
     //   rd.poll(c)  starts looking at chunk c (no wait),
     //   rd.wait(c)  returns once chunk c's record may be read; false if it never
     //               became ready (the chain then stops and writes NaN state),
-    // and reaches the other waves through LDS (one slot per chunk parity).
-    // Chunk c + 2's readiness is polled before chunk c's arithmetic and awaited
-    // after it, so that chunk c + 1's copies can start right after chunk c's
-    // first barrier and the flag's latency hides behind the arithmetic.
+    // and reaches the other waves through LDS (one slot per chunk parity).  One
+    // workgroup barrier per chunk: past it, chunk c's copies are in LDS, every
+    // wave is done with chunk c - 1 (so its stage takes chunk c + 1's copies),
+    // and chunk c + 1's readiness is in its slot.  Chunk c + 2's readiness is
+    // awaited while the compute waves work on chunk c.
     template <typename Ready>
     __device__ __forceinline__ void run(const FwdParams& p, const unsigned char* rec0, size_t RB, int NC, int bh,
                                         size_t tok_base, int colbase, Ready& rd) {
-        const int col0 = colbase + 16 * SPW * wave;          // this wave's first column
         int* s_ok = reinterpret_cast<int*>(smem + L::oOk);   // [2]: chunk x's readiness in slot x & 1
-        floatx4 S[SPW][NKT];
-#pragma unroll
-        for (int s = 0; s < SPW; ++s)
-#pragma unroll
-            for (int mt = 0; mt < NKT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[s][mt][i] = p.S0 ? p.S0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col0 + 16 * s + n_l] : 0.f;
-        const bool out_bf16 = (p.flags & GDR_OUT_BF16) != 0;
         bool ok = NC > 0;
         if (NC > 0) {
-            if (wave == 0) {
+            if (wave == kComputeWaves) {
                 rd.poll(0);
                 const bool r0 = rd.wait(0);
                 bool r1 = true;
@@ -842,23 +837,53 @@ struct Chain {
             }
             lds_barrier();
             ok = s_ok[0] != 0;
-            if (ok) fetch(rec0, 0);
         }
+        if (wave < kComputeWaves) compute(p, rec0, NC, bh, tok_base, colbase, ok);
+        else copy(rec0, RB, NC, ok, rd);
+        lds_barrier();                                         // LDS free for the next chain
+    }
+
+    template <typename Ready>
+    __device__ __forceinline__ void copy(const unsigned char* rec0, size_t RB, int NC, bool ok, Ready& rd) {
+        int* s_ok = reinterpret_cast<int*>(smem + L::oOk);
+        if (ok) fetch(rec0, 0);
         for (int c = 0; c < NC && ok; ++c) {
-            // this wave's copies of chunk c have landed (the only younger vector
-            // memory operations are the output stores of chunk c - 1)
-            if (c == 0) wait_vm<0>();
-            else wait_vm<4 * SPW>();
-            // every wave's copies of chunk c are in; every wave is past chunk c - 1,
-            // so stage (c + 1) & 1 is free; chunk c + 1's readiness is in its slot
+            wait_vm<0>();                                      // this wave's copies of chunk c
             lds_barrier();
-            if (c + 1 < NC) {
-                if (s_ok[(c + 1) & 1] == 0) {
-                    ok = false;
-                    break;
-                }
-                fetch(rec0 + (size_t)(c + 1) * RB, (c + 1) & 1);
-                if (wave == 0 && c + 2 < NC) rd.poll(c + 2);
+            if (c + 1 < NC && s_ok[(c + 1) & 1] == 0) {
+                ok = false;
+                break;
+            }
+            if (c + 1 < NC) fetch(rec0 + (size_t)(c + 1) * RB, (c + 1) & 1);
+            // chunk c + 2's readiness into slot c & 1 (read after the next barrier;
+            // its previous readers, past the barrier of chunk c - 1, are past this one)
+            if (wave == kComputeWaves && c + 2 < NC) {
+                rd.poll(c + 2);
+                const bool r = rd.wait(c + 2);
+                if (lane == 0) s_ok[c & 1] = r ? 1 : 0;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void compute(const FwdParams& p, const unsigned char* rec0, int NC, int bh,
+                                            size_t tok_base, int colbase, bool ok) {
+        (void)rec0;
+        const int col0 = colbase + 16 * SPW * wave;          // this wave's first column
+        int* s_ok = reinterpret_cast<int*>(smem + L::oOk);
+        floatx4 S[SPW][NKT];
+#pragma unroll
+        for (int s = 0; s < SPW; ++s)
+#pragma unroll
+            for (int mt = 0; mt < NKT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[s][mt][i] = p.S0 ? p.S0[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col0 + 16 * s + n_l] : 0.f;
+        const bool out_bf16 = (p.flags & GDR_OUT_BF16) != 0;
+        for (int c = 0; c < NC && ok; ++c) {
+            lds_barrier();
+            if (c + 1 < NC && s_ok[(c + 1) & 1] == 0) {
+                ok = false;
+                break;
             }
             const unsigned char* st = smem + (size_t)(c & 1) * L::stage;
             auto frag = [&](size_t off) __attribute__((always_inline)) {
@@ -992,12 +1017,6 @@ struct Chain {
                         *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(p.o) + base) = o;
                     }
                 }
-            // chunk c + 2's readiness into its slot (read after the next barrier;
-            // its previous reader, chunk c - 1's iteration, is past this one's barrier)
-            if (wave == 0 && c + 2 < NC) {
-                const bool r = rd.wait(c + 2);
-                if (lane == 0) s_ok[c & 1] = r ? 1 : 0;
-            }
         }
         if (p.Sf) {
 #pragma unroll
@@ -1009,7 +1028,6 @@ struct Chain {
                         p.Sf[((size_t)bh * DK + 16 * mt + g4 + i) * DV + col0 + 16 * s + n_l] =
                             ok ? S[s][mt][i] : __builtin_nanf("");
         }
-        lds_barrier();                                         // LDS free for the next chain
     }
 };
 
