@@ -2,10 +2,11 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
 Headline: the chunkwise Gated DeltaNet-2 forward (gate prep and intra-chunk
-WY operands for all chunks in parallel, then the inter-chunk state pass with
+WY operands for all chunks in parallel, and the inter-chunk state pass with
 the output) at B=2, H=16, T=8192, d_k=d_v=128, chunk 64, bf16 activations,
 fp32 log-decay and state.  One step = one gdr_chunk_fwd call over that batch
-(two kernel launches, with a workspace), inputs resident in HBM.
+(a flag-clearing launch, then one persistent kernel whose producer and chain
+workgroups run side by side, with a workspace), inputs resident in HBM.
 value = B*H*T head-tokens per second of wall time over the timed steps.
 
 Also reported in the same JSON line: the recurrent decode step (256
@@ -13,7 +14,7 @@ sequences x 32 heads, fp32 state streamed in place) in GB/s, the same
 forward over packed documents of varied lengths, the backward
 (1 x 32 heads x 16384 tokens), the roofline position of the forward call
 (the method's algorithmic HBM bytes per call over the measured call
-duration, with the measured HBM traffic of both kernels), and the fp64 CPU
+duration, with the measured HBM traffic of the call), and the fp64 CPU
 oracle timed on this host as a reference baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -87,12 +88,12 @@ BB, BH_, BT = 1, 32, 16384
 BWD_BYTES_PER_TOKEN = 6 * FD * 2 + FD * 4 + 6 * FD * 4
 BWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
 
-# the timed call runs the two-pass kernels (WY operands, then the state chain);
-# the counters in the traffic summary are only used while these sources are
-# unchanged
-FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_wy.hip",
+# the timed call runs the persistent producer/chain kernel; the counters in
+# the traffic summary are only used while these sources are unchanged
+FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_fz.hip",
                       "gated_delta_rule_24_amd/csrc/gdr_wy.h",
-                      "gated_delta_rule_24_amd/csrc/gdr_device.h"]
+                      "gated_delta_rule_24_amd/csrc/gdr_device.h",
+                      "gated_delta_rule_24_amd/csrc/gdr_launch.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
 
 
@@ -605,7 +606,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "scope": "one gdr_chunk_fwd call: wy_kernel + chain_kernel",
+            "scope": "one gdr_chunk_fwd call: fz_clear + fused_kernel (producer and chain roles)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
