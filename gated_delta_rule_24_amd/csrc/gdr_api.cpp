@@ -268,7 +268,7 @@ gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* 
     const uint32_t gate_modes = GDR_ALPHA_SCALAR | GDR_B_SCALAR | GDR_W_SCALAR | GDR_GATE_LOGITS;
     if (flags & ~(kKnownFlags & ~GDR_OUT_BF16 & ~GDR_FWD_GENERIC)) return GDR_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || T < 0) return GDR_ERR_INVALID_ARG;
-    if ((long long)B * H > (1LL << 28) || (long long)B * H * ((T + 63) / 64) > (1LL << 31) - 1)
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * (((long long)T + 63) / 64) > (1LL << 31) - 1)
         return GDR_ERR_INVALID_ARG;
     if (!gdr::mixer_supported(d_k) || !gdr::mixer_supported(d_v) || (flags & ~gate_modes))
         return GDR_ERR_UNSUPPORTED;
@@ -314,7 +314,7 @@ gdr_status gdr_mixer_epilogue(const float* o, const void* g, const float* norm_w
 
 size_t gdr_mixer_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v) {
     if (B < 1 || H < 1 || T < 1 || d_k != d_v || !gdr::mixer_supported(d_k)) return 0;
-    if ((long long)B * H > (1LL << 28) || (long long)B * H * ((T + 63) / 64) > (1LL << 31) - 1) return 0;
+    if ((long long)B * H > (1LL << 28) || (long long)B * H * (((long long)T + 63) / 64) > (1LL << 31) - 1) return 0;
     const size_t pro = gdr::mixer_prologue_bwd_workspace_bytes(B * H, T, d_k, d_v);
     const size_t epi = gdr::mixer_epilogue_bwd_workspace_bytes(d_v);
     return pro > epi ? pro : epi;

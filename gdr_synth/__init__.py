@@ -223,7 +223,7 @@ def packed_lengths(n: int, mean: int, seed: int = 0, lo: int = 1) -> list:
 
 
 # decode workload: 256 sequences x 32 heads, d=128, fp32 state from N(0, 0.02)
-DECODE = dict(N=256, H=32, dk=128, dv=128)
+DECODE = dict(N=256, H=32, dk=128, dv=128, steps=128)
 
 
 def decode_state(N: int, H: int, dk: int, dv: int, seed: int = 0, std: float = 0.02) -> np.ndarray:

@@ -75,8 +75,10 @@ def test_decode_bf16_output_is_rounded_fp32_output():
 
 
 def test_decode_full_workload_sampled():
-    """256 sequences x 32 heads, d=128, 8 steps: every head after step 1 and
-    a sample of 64 heads followed over all steps."""
+    """The decode workload: 256 sequences x 32 heads, d=128, fp32 state updated
+    in place over its 128 steps.  Every head is checked after step 1, and a
+    sample of 64 heads is followed over all 128 steps (output of every step,
+    state at the end)."""
     import torch
     import gated_delta_rule_24_amd as gdr
     N, H = gs.DECODE["N"], gs.DECODE["H"]
@@ -86,7 +88,7 @@ def test_decode_full_workload_sampled():
     rng = np.random.default_rng(5)
     pick = rng.choice(N * H, size=64, replace=False)
     Sref = S.reshape(N * H, d, d)[pick].astype(np.float64)
-    for step in range(8):
+    for step in range(gs.DECODE["steps"]):
         tok = gs.decode_token(N, H, d, d, step, seed=0)
         dv = _dev(tok, "bf16")
         o = gdr.decode_step(dv["q"], dv["k"], dv["v"], dv["log_alpha"], dv["b"], dv["w"], Sd)
