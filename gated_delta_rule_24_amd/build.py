@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libgdr.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_fwd_wy.hip", "gdr_bwd_wy.hip", "gdr_mixer.hip",
-           "gdr_bwd.hip", "gdr_noalloc.hip", "gdr_fwd_fz.hip"]
+           "gdr_bwd.hip", "gdr_noalloc.hip", "gdr_fwd_fz.hip", "gdr_exact.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 

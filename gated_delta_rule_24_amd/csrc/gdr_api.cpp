@@ -39,6 +39,15 @@ gdr_status check_device() {
     return known[dev] == 1 ? GDR_OK : GDR_ERR_DEVICE;
 }
 
+// A backward workspace also holds, after the chunk kernels are done with it,
+// one slot of the token-by-token recompute (checkpoints every 64 tokens and one
+// segment's states), for the heads whose decay left the chunk kernels' range.
+size_t bwd_need(size_t fast, int T, int d_k, int d_v) {
+    if (fast == 0 || T <= 0) return fast;
+    const size_t slot = gdr::exact_bwd_slot_bytes(T, d_k, d_v);
+    return fast > slot ? fast : slot;
+}
+
 gdr_status from_hip(hipError_t e) {
     if (e == hipSuccess) return GDR_OK;
     if (e == hipErrorInvalidValue) return GDR_ERR_UNSUPPORTED;
@@ -100,7 +109,10 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.BH = B * H; p.T = T; p.flags = flags;
     if (two_pass) return from_hip(gdr::launch_fwd_fz(p, d_k, d_v, workspace, (hipStream_t)stream));
     int used = 0;
-    return from_hip(gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used));
+    const hipError_t e = gdr::launch_fwd(p, d_k, d_v, chunk, (hipStream_t)stream, &used);
+    if (e != hipSuccess) return from_hip(e);
+    // heads whose decay left the chunk kernel's operand range: token by token
+    return from_hip(gdr::launch_exact_fwd(p, d_k, d_v, (hipStream_t)stream));
 }
 
 size_t gdr_chunk_fwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v,
@@ -137,7 +149,10 @@ gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
     p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
     p.cu_seqlens = cu_seqlens; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = nseq;
     p.BH = H; p.T = T; p.flags = flags;
-    return from_hip(gdr::launch_fwd_wy_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
+    const hipError_t e = gdr::launch_fwd_wy_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    // sequences whose decay left the chunk kernels' operand range: token by token
+    return from_hip(gdr::launch_exact_fwd(p, d_k, d_v, (hipStream_t)stream));
 }
 
 gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -165,7 +180,7 @@ size_t gdr_chunk_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int 
     if (B < 1 || H < 1 || T < 0 || !(chunk == 16 || chunk == 32 || chunk == 64)) return 0;
     if (T % chunk != 0 || !sizes_ok(B, H, T)) return 0;
     if (!gdr::bwd_supported(d_k, d_v, chunk, flags)) return 0;
-    return gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
+    return bwd_need(gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags), T, d_k, d_v);
 }
 
 gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -191,7 +206,7 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
     if ((flags & GDR_GATE_LOGITS) && T > 0 && !gdr::bwd_two_pass_supported(d_k, d_v, chunk, flags))
         return GDR_ERR_UNSUPPORTED;
     const size_t need = gdr::bwd_workspace_bytes(B * H, T, d_k, d_v, chunk, flags);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || workspace_bytes < bwd_need(need, T, d_k, d_v))) return GDR_ERR_WORKSPACE;
     gdr_status ds = check_device();
     if (ds != GDR_OK) return ds;
 
@@ -214,13 +229,17 @@ gdr_status gdr_chunk_bwd(const void* q, const void* k, const void* v, const floa
         p.dstate_frags = base + sb;
         if (need > 2 * sb) p.records = base + 2 * sb;
     }
-    return from_hip(gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream));
+    const hipError_t e = gdr::launch_bwd(p, d_k, d_v, chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    // heads whose decay left the chunk kernels' operand range: token by token,
+    // in the workspace the chunk kernels are done with
+    return from_hip(gdr::launch_exact_bwd(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 size_t gdr_chunk_bwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int d_v, uint32_t flags) {
     if (nseq < 1 || H < 1 || T < 0 || (long long)nseq * H > (1LL << 28)) return 0;
     if ((flags & ~(kKnownFlags & ~GDR_OUT_BF16)) || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return 0;
-    return gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    return bwd_need(gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v), T, d_k, d_v);
 }
 
 gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -243,7 +262,7 @@ gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
     if ((long long)nseq * H > (1LL << 28) || (long long)H * (T / 64 + nseq) > (1LL << 30))
         return GDR_ERR_INVALID_ARG;
     if (d_k != d_v || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return GDR_ERR_UNSUPPORTED;
-    const size_t need = gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    const size_t need = bwd_need(gdr::bwd_varlen_workspace_bytes(H, T, nseq, d_k, d_v), T, d_k, d_v);
     if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
     gdr_status ds = check_device();
     if (ds != GDR_OK) return ds;
@@ -257,7 +276,10 @@ gdr_status gdr_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
     p.cu_seqlens = cu_seqlens; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr;
     p.nseq = nseq;
     p.BH = H; p.T = T; p.flags = flags;
-    return from_hip(gdr::launch_bwd_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
+    const hipError_t e = gdr::launch_bwd_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    // sequences whose decay left the chunk kernels' operand range: token by token
+    return from_hip(gdr::launch_exact_bwd(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 gdr_status gdr_mixer_prologue(const void* q_pre, const void* k_pre, const void* v_pre,

@@ -142,6 +142,16 @@ struct BwdParams {
 };
 
 size_t bwd_workspace_bytes(int BH, int T, int dk, int dv, int chunk, uint32_t flags);
+
+// Token-by-token recompute (gdr_exact.hip) of the units (fixed-length heads,
+// or packed (sequence, head) pairs) whose chunkwise results are NaN because a
+// chunk's decay left the operand range: the forward rewrites o and S_final,
+// the backward every gradient.  Clean units cost one marker read.  The
+// backward needs exact_bwd_slot_bytes() of workspace per unit processed at
+// once (it processes as many as fit, at least one).
+size_t exact_bwd_slot_bytes(int T, int dk, int dv);
+hipError_t launch_exact_fwd(const FwdParams& p, int dk, int dv, hipStream_t st);
+hipError_t launch_exact_bwd(const BwdParams& p, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st);
 // Reverse state-gradient chain over the records of launch_fwd_wy(..., bwd_layouts = true).
 hipError_t launch_bwd_dchain(const BwdParams& p, int dk, int dv, const void* records, hipStream_t st);
 // Per-chunk gradients over those records and the f16 state fragments.

@@ -107,27 +107,38 @@ def test_decode_argument_validation():
     assert call(dk=48) == 2
 
 
+def _exact(T, dk, dv):
+    """Workspace of one unit of the backward's token-by-token recompute (run for
+    heads whose decay leaves the chunk kernels' operand range): fp32 state
+    checkpoints every 64 tokens, then the states of one 64-token segment."""
+    return ((T + 63) // 64 + 64) * dk * dv * 4
+
+
 def test_bwd_workspace_query_and_validation():
     lib = _lib()
+    q = lib.gdr_chunk_bwd_workspace_bytes
     # the two-pass path: decayed chunk-start states and chunk-end gradients as f16
     # (2 x B*H x T/chunk x d_k x d_v x 2 bytes), plus the forward's records, each
     # extended by three 64 x d_k and two 64 x 64 f16 operand layouts for the
-    # backward passes
+    # backward passes; at least one unit of the token-by-token recompute
     states = 2 * 2 * 2 * 128 * 128 * 2
     # the backward's own records: W, Kh^T, U', Q', P (f16) and the decay slot
     records = 2 * 2 * (4 * 64 * 128 * 2 + 64 * 64 * 2 + 768)
     extra = 2 * 2 * (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2)
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 64, 0) == states + records + extra
+    assert q(1, 2, 128, 128, 128, 64, 0) == max(states + records + extra, _exact(128, 128, 128))
+    per_chunk = (states + records + extra) // 4
+    assert q(1, 2, 64 * 64, 128, 128, 64, 0) == 2 * 64 * per_chunk          # chunk records dominate
     # fp32 activations block the backward with chunks of 32
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 64, 1) == 2 * 2 * 4 * 64 * 64 * 4
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 128, 48, 0) == 0
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 96, 64, 0) == 0
+    assert q(1, 2, 128, 64, 64, 64, 1) == max(2 * 2 * 4 * 64 * 64 * 4, _exact(128, 64, 64))
+    assert q(1, 2, 128, 128, 128, 48, 0) == 0
+    assert q(1, 2, 128, 128, 96, 64, 0) == 0
     # other head shapes and chunks run the generic path: fp32 chunk-start states
     # and chunk-end gradients (2 x B*H x T/chunk x d_k x d_v x 4 bytes)
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 32, 32, 64, 0) == 2 * 2 * 2 * 32 * 32 * 4
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 128, 64, 64, 0) == 2 * 2 * 2 * 128 * 64 * 4
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 16, 128, 16, 0) == 2 * 2 * 8 * 16 * 128 * 4
-    assert lib.gdr_chunk_bwd_workspace_bytes(1, 2, 128, 64, 64, 16, 1) == 2 * 2 * 8 * 64 * 64 * 4
+    assert q(1, 2, 128, 32, 32, 64, 0) == max(2 * 2 * 2 * 32 * 32 * 4, _exact(128, 32, 32))
+    assert q(1, 2, 128, 128, 64, 64, 0) == max(2 * 2 * 2 * 128 * 64 * 4, _exact(128, 128, 64))
+    assert q(1, 2, 128, 16, 128, 16, 0) == max(2 * 2 * 8 * 16 * 128 * 4, _exact(128, 16, 128))
+    assert q(1, 2, 128, 64, 64, 16, 1) == max(2 * 2 * 8 * 64 * 64 * 4, _exact(128, 64, 64))
+    assert q(4, 8, 1 << 14, 32, 32, 16, 0) == 2 * 32 * 1024 * 32 * 32 * 4
 
     def call(ws=A, nbytes=1 << 30, **kw):
         a = dict(B=1, H=2, T=128, dk=128, dv=128, chunk=64, flags=0)
@@ -207,18 +218,19 @@ def test_bwd_varlen_argument_validation(kw, status):
 
 def test_bwd_varlen_workspace_query():
     lib = _lib()
+    q = lib.gdr_chunk_bwd_varlen_workspace_bytes
     # per chunk slot (H * (T//64 + nseq) of them): the forward record with the
     # backward's layouts, S' and the state gradient as f16 (2 x d_k x d_v x 2
-    # bytes); then the prep arrays as for the packed forward
-    rec = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0) - 2 * 128 * 128 * 2
-    slot = rec + 2 * 128 * 128 * 2
-    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(3, 2, 200, 128, 128, 0) == 2 * 6 * slot + 768
-    rec64 = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0) - 2 * 64 * 64 * 2
-    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 4, 128, 64, 64, 0x1c) == \
-        4 * 3 * (rec64 + 2 * 64 * 64 * 2) + 768
-    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 64, 0) == 0
-    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0
-    assert lib.gdr_chunk_bwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
+    # bytes); then the prep arrays as for the packed forward; at least one unit
+    # of the token-by-token recompute over T tokens
+    slot = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64 * 64, 128, 128, 64, 0) // 64
+    assert q(3, 2, 200, 128, 128, 0) == max(2 * 6 * slot + 768, _exact(200, 128, 128))
+    assert 2 * 67 * slot < q(3, 2, 64 * 64, 128, 128, 0) < 2 * 67 * slot + 4096   # chunk slots dominate
+    slot64 = lib.gdr_chunk_bwd_workspace_bytes(1, 1, 64 * 64, 64, 64, 64, 0) // 64
+    assert q(1, 4, 128, 64, 64, 0x1c) == max(4 * 3 * slot64 + 768, _exact(128, 64, 64))
+    assert q(1, 1, 64, 128, 64, 0) == 0
+    assert q(1, 1, 64, 128, 128, 0x1) == 0
+    assert q(0, 1, 64, 128, 128, 0) == 0
 
 
 def test_mixer_argument_validation():

@@ -165,12 +165,27 @@ def test_backward_empty_sequence_passes_state_gradient():
     assert torch.count_nonzero(g["dS0"]).item() == 0
 
 
-def test_backward_decay_beyond_f16_range_is_loud():
-    """A chunk whose in-chunk decay exceeds the f16 operand range yields NaN
-    gradients (never silently wrong values)."""
-    inp = _case("strong", B=1, H=1, T=128, dk=64, dv=64, decay_scale=1.0)
-    g = _run(inp)
-    assert np.isnan(g["dq"]).any() and np.isnan(g["dS0"]).any()
+STRONG = [
+    # name, kwargs, tol: decay_scale s gives about 0.8 s nats per token
+    ("channel_0.5_d128", dict(B=1, H=2, T=256, dk=128, dv=128, decay_scale=0.5), 2e-2),
+    ("channel_2_d128", dict(B=1, H=2, T=256, dk=128, dv=128, decay_scale=2.0), 2e-2),
+    ("gdn_sigmoid_gate_d128", dict(B=1, H=2, T=256, dk=128, dv=128, alpha_mode="scalar", b_mode="scalar",
+                                   w_mode="scalar", tied=True, decay_scale=1.0), 2e-2),
+    ("channel_2_d64_c32", dict(B=2, H=1, T=192, dk=64, dv=64, decay_scale=2.0, chunk=32), 2e-2),
+    ("channel_2_dk128_dv64", dict(B=1, H=2, T=128, dk=128, dv=64, decay_scale=2.0), 2e-2),
+    ("channel_2_f32_d64", dict(B=1, H=2, T=128, dk=64, dv=64, decay_scale=2.0, act="f32"), 1e-4),
+    ("channel_20_d64", dict(B=1, H=1, T=128, dk=64, dv=64, decay_scale=20.0), 2e-2),
+]
+
+
+@pytest.mark.parametrize("name,kw,tol", STRONG, ids=[c[0] for c in STRONG])
+def test_strong_decay_backward(name, kw, tol):
+    """Decay beyond the chunk kernels' operand range: those heads' gradients
+    are recomputed token by token in fp32 and match the oracle (values, not
+    NaN), with dS_final given."""
+    inp = _case(name, **kw)
+    dSf = _dsf(inp)
+    _check(inp, _run(inp, dSf), _ref(inp, dSf), tol)
 
 
 def test_gdn2_backward_full_workload_all_heads():

@@ -123,6 +123,10 @@ CASES = [
     ("zero_initial_state", [40, 200], dict(H=2, dk=64, dv=64, s0_std=None), True),
     ("one_long", [1000], dict(H=1, dk=128, dv=128), True),
     ("all_single_tokens", [1] * 37, dict(H=2, dk=64, dv=64), True),
+    # decay beyond the chunk kernels' operand range: recomputed token by token
+    ("strong_decay", [150, 77, 1, 0, 64], dict(H=2, dk=128, dv=128, decay_scale=2.0), True),
+    ("strong_decay_gdn_d64", [90, 33], dict(H=2, dk=64, dv=64, alpha_mode="scalar", b_mode="scalar",
+                                          w_mode="scalar", tied=True, decay_scale=1.0), False),
 ]
 
 

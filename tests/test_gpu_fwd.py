@@ -253,16 +253,43 @@ def test_strong_decay_two_pass(name, kw):
     _check(inp, o, sf, 2e-2)
 
 
-def test_decay_beyond_f16_range_is_loud_on_the_fused_path():
-    """Without a workspace the single fused kernel runs; it references a
-    chunk's decay to the chunk end, and a chunk whose accumulated decay exceeds
-    the f16 operand range poisons its head's outputs with NaN instead of
-    returning wrong numbers."""
-    import torch
-    inp = _case("strong", B=1, H=2, T=128, dk=64, dv=64, decay_scale=2.0)
+STRONG_FUSED = STRONG + [
+    ("channel_2_f32", dict(B=1, H=2, T=128, dk=64, dv=64, decay_scale=2.0, act="f32")),
+    ("channel_2_d32x16_c16", dict(B=2, H=1, T=96, dk=32, dv=16, decay_scale=2.0, chunk=16)),
+]
+
+
+@pytest.mark.parametrize("name,kw", STRONG_FUSED, ids=[c[0] for c in STRONG_FUSED])
+def test_strong_decay_single_kernel(name, kw):
+    """Without a workspace the single-kernel forward runs; it references a
+    chunk's decay to the chunk's end, and a head whose decay leaves its
+    operand range is recomputed token by token in fp32, so the outputs are
+    values for any decay (tolerance 1e-4 with fp32 activations)."""
+    inp = _case(name, **kw)
     o, sf = _run(inp, path="fused")
-    assert torch.isnan(sf).any()
-    assert torch.isnan(o).any()
+    _check(inp, o, sf, 1e-4 if inp.act == "f32" else 2e-2)
+
+
+def test_strong_decay_leaves_other_heads_to_the_chunk_kernel():
+    """One head with strong decay among heads within range: the token-level
+    recompute rewrites that head only; the others keep the chunk kernel's
+    result bit for bit."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    from tests.helpers import to_dev
+    inp = _case("mixed_heads", B=1, H=3, T=192, dk=64, dv=64)
+    strong = gs.make_inputs(1, 1, 192, 64, 64, decay_scale=2.0, seed=9)
+    inp.arrays["log_alpha"][:, 1] = strong.arrays["log_alpha"][:, 0]
+    d = to_dev(inp)
+    o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], path="fused")
+    torch.cuda.synchronize()
+    _check(inp, o, sf, 2e-2)
+    # heads 0 and 2 alone, with the same inputs
+    keep = [0, 2]
+    d2 = {n: (None if t is None else t[:, keep].contiguous()) for n, t in d.items()}
+    o2, s2 = gdr.chunk_fwd(d2["q"], d2["k"], d2["v"], d2["log_alpha"], d2["b"], d2["w"], d2["S0"], path="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, keep], o2) and torch.equal(sf[:, keep], s2)
 
 
 @pytest.mark.parametrize("name,kw", [
