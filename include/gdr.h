@@ -49,6 +49,13 @@
  *   one key repeated through a chunk with an erase gate near 2 makes the
  *   in-chunk solve cancel by about two orders of magnitude, and such inputs
  *   need fp32 activations.
+ * - Decay range: every call returns values for any decay an fp32 log_alpha
+ *   can express.  The persistent forward references each 16-token block's
+ *   decay so that no operand factor exceeds 1.  The other chunk kernels
+ *   reference a chunk's decay to its end; a (sequence, head) whose in-chunk
+ *   decay leaves their operand range (about 10 nats per chunk with f16
+ *   operands) is recomputed token by token in fp32 by a follow-up kernel of
+ *   the same call, which costs one small launch when no head needs it.
  */
 #ifndef GDR_H
 #define GDR_H
