@@ -25,13 +25,20 @@
 //   row operands  b⊙k⊙e^{g_r - rr_R},  q⊙e^{g_r - rr_R}      (r in block R)
 //   col operands  k⊙e^{cr_I - g_i}                            (i in block I)
 // and a tile (R, I), R > I, rescales the col operand by e^{rr_R - cr_I}.
-// A block whose in-block decay is moderate takes its middle token as both
-// references (rr = cr = g at token 7 of the block; every factor within
-// e^{±kMidLimit}), so its diagonal tile needs no rescaling.  A block with
-// stronger decay references its ends (rr = g before its first token, cr = g
-// at its last token; every factor <= 1) and forms its diagonal tile from the
-// exact per-element factors e^{g_r - g_i} in fp32.  In both cases
-// rr_R <= cr_I for R > I, so the rescaling factor never exceeds 1.
+// A block whose tokens all lie within kMidLimit of the chunk's middle token
+// (g at token C/2 - 1) takes that token as both references; blocks of this
+// kind share one reference, so their tiles need no rescaling (the usual case:
+// a chunk's whole decay is a few nats).  Otherwise a block whose in-block
+// decay is moderate takes its own middle token as both references (rr = cr =
+// g at token 7 of the block; every factor within e^{±kMidLimit}), so its
+// diagonal tile needs no rescaling.  A block with stronger decay references
+// its ends (rr = g before its first token, cr = g at its last token; every
+// factor <= 1) and forms its diagonal tile from the exact per-element factors
+// e^{g_r - g_i} in fp32.  With log alpha <= 0 (g never increases) a rescaled
+// col operand k_i e^{rr_R - g_i} stays within e^{kMidLimit} of k_i: the
+// factor exceeds 1 only when R takes the chunk's middle and I (< R) its own,
+// and then every token of R, so every earlier token, lies above
+// rr_R - kMidLimit.
 //
 // The producer writes each chunk's record (W, Kh^T, U', Q_s, P as MFMA
 // fragments, then e^{g_C}) to the workspace; the chain keeps the state in
@@ -64,6 +71,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // this many nats of the block's middle (factors within e^{±6} keep f16 normal
 // for inputs down to about 0.01)
 constexpr float kMidLimit = 6.0f * kLog2e;   // in log2 units
+// a 16-token block's reference for its A and P operands (see Producer::chunk)
+constexpr int kRefBlock = 0, kRefEnds = 1, kRefChunk = 2;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -111,7 +120,8 @@ struct ProdLayout {
     static constexpr size_t oK = oQ + (size_t)C * LDE * 2;
     static constexpr size_t oEt = oK + (size_t)C * LDE * 2;      // E_s^T [DK][LDT2]
     static constexpr size_t oXt = oEt + (size_t)DK * LDT2 * 2;   // X^T   [DV][LDT2]
-    static constexpr size_t oT = (oXt + (size_t)DV * LDT2 * 2 + 15) & ~size_t(15);
+    static constexpr size_t oKt = oXt + (size_t)DV * LDT2 * 2;   // Kh^T  [DK][LDT2]
+    static constexpr size_t oT = (oKt + (size_t)DK * LDT2 * 2 + 15) & ~size_t(15);
     static constexpr size_t oP = oT + (size_t)C * LDT * 2;
     static constexpr size_t oZ = oP + (size_t)C * LDT * 2;       // Z^T [C/2][LDT]
     static constexpr size_t oA = oZ + (size_t)(C / 2) * LDT * 2;
@@ -121,6 +131,7 @@ struct ProdLayout {
     static constexpr size_t oFl = oAd + (size_t)(C / 16) * 16 * LDD * 4;   // [NW] int
     static constexpr size_t bytes = oFl + (size_t)NW * 4;
     static_assert(PW * TPP == 16, "a wave holds one block");
+    static_assert(TPP % 2 == 0 && XTP % 2 == 0, "per-token gates are loaded two tokens at a time");
 };
 
 // the channel of slot i (0..7) of channel group co: two runs of four, in the
@@ -148,6 +159,7 @@ struct Producer {
     bool BS, WS;            // b, w one value per token (GDR_B_SCALAR, GDR_W_SCALAR)
     // raw inputs of one chunk (issued one chunk ahead, in three groups)
     uint2 rq[TPP][2], rk[TPP][2], rb[TPP][2];
+    uint32_t rbs[TPP / 2], rws[XTP / 2];   // b, w of one value per token: two tokens' bf16 per word
     floatx4 rla[TPP][2];
     u32x4 rv[XTP], rw[XTP];
 
@@ -156,6 +168,7 @@ struct Producer {
     __device__ __forceinline__ _Float16* sK() { return reinterpret_cast<_Float16*>(smem + L::oK); }
     __device__ __forceinline__ _Float16* sEt() { return reinterpret_cast<_Float16*>(smem + L::oEt); }
     __device__ __forceinline__ _Float16* sXt() { return reinterpret_cast<_Float16*>(smem + L::oXt); }
+    __device__ __forceinline__ _Float16* sKt() { return reinterpret_cast<_Float16*>(smem + L::oKt); }
     __device__ __forceinline__ _Float16* sT() { return reinterpret_cast<_Float16*>(smem + L::oT); }
     __device__ __forceinline__ _Float16* sP() { return reinterpret_cast<_Float16*>(smem + L::oP); }
     __device__ __forceinline__ _Float16* sZ() { return reinterpret_cast<_Float16*>(smem + L::oZ); }
@@ -188,9 +201,15 @@ struct Producer {
         }
     }
 
-    // the loads of a chunk's inputs, group 0 (q, k), 1 (b, log alpha), 2 (v, w)
+    // the loads of a chunk's inputs, group 0 (q, k), 1 (b, log alpha), 2 (v, w).
+    // Both forms of b and w are loaded whatever the gate mode: the per-token
+    // value (in bounds in either layout) and eight channels, which with one
+    // value per token come from k or v instead (same shape, never used).  The
+    // loads then take no branch, so no loaded register is copied (a copy would
+    // wait for every load in flight).
     __device__ __forceinline__ void issue(const FwdParams& p, size_t tok0, int group) {
         const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b);
+        const uint16_t* bv = BS ? reinterpret_cast<const uint16_t*>(p.k) : bg;
         if (group < 2) {
             const int c0 = grp_ch(co, 0), c1 = grp_ch(co, 4);
 #pragma unroll
@@ -205,12 +224,9 @@ struct Producer {
                     rk[j][0] = *reinterpret_cast<const uint2*>(kg + c0);
                     rk[j][1] = *reinterpret_cast<const uint2*>(kg + c1);
                 } else {
-                    if (BS) {
-                        rb[j][0].x = bg[t];
-                    } else {
-                        rb[j][0] = *reinterpret_cast<const uint2*>(bg + ix + c0);
-                        rb[j][1] = *reinterpret_cast<const uint2*>(bg + ix + c1);
-                    }
+                    if (j % 2 == 0) rbs[j / 2] = *reinterpret_cast<const uint32_t*>(bg + t);
+                    rb[j][0] = *reinterpret_cast<const uint2*>(bv + ix + c0);
+                    rb[j][1] = *reinterpret_cast<const uint2*>(bv + ix + c1);
                     if constexpr (AS) {
                         rla[j][0][0] = p.la[t];
                     } else {
@@ -222,13 +238,14 @@ struct Producer {
         } else {
             const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v);
             const uint16_t* wg = reinterpret_cast<const uint16_t*>(p.w);
+            const uint16_t* wv = WS ? vg : wg;
 #pragma unroll
             for (int j = 0; j < XTP; ++j) {
                 const size_t t = tok0 + xpart * XTP + j;
                 const size_t ix = t * DV + 8 * vo;
                 rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
-                if (WS) rw[j][0] = wg[t];
-                else rw[j] = *reinterpret_cast<const u32x4*>(wg + ix);
+                rw[j] = *reinterpret_cast<const u32x4*>(wv + ix);
+                if (j % 2 == 0) rws[j / 2] = *reinterpret_cast<const uint32_t*>(wg + t);
             }
         }
     }
@@ -245,7 +262,7 @@ struct Producer {
     }
     __device__ __forceinline__ void gate_b(int j, float (&b8)[8]) const {
         if (BS) {
-            float bs = __uint_as_float(rb[j][0].x << 16);
+            float bs = __uint_as_float(j % 2 == 0 ? rbs[j / 2] << 16 : rbs[j / 2] & 0xffff0000u);
             if (LG) bs = gate_sigmoid(bs);
 #pragma unroll
             for (int i = 0; i < 8; ++i) b8[i] = bs;
@@ -312,11 +329,12 @@ struct Producer {
         const NextItem nx = hook.after();
         const bool has_next = nx.has;
         const size_t ntok0 = nx.tok0;
-        float base[8], wtot[8], gC[8], mid[8];
+        float base[8], wtot[8], gC[8], mid[8], gM[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             base[i] = 0.f;
             gC[i] = 0.f;
+            gM[i] = 0.f;
         }
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2)
@@ -325,6 +343,7 @@ struct Producer {
                 const float t = tot[w2 * DK + grp_ch(co, i)];
                 if (w2 < wave) base[i] += t;
                 if (w2 == wave) wtot[i] = t;
+                if (w2 < NW / 2) gM[i] += t;          // g at the chunk's middle token (C/2 - 1)
                 gC[i] += t;
             }
         // g at every token, and at token 7 of this wave's block (the lane of the
@@ -341,19 +360,28 @@ struct Producer {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) gl[j][i] += base[i] + excl[i];
         }
-        // the block's reference: its middle token, unless a token lies farther
-        // from it than kMidLimit (then its two ends)
-        bool far = false;
+        // the block's reference (its mode, kept in sFl for the tile phase):
+        //   kRefChunk  the chunk's middle token, when every token of the block lies
+        //              within kMidLimit of it (blocks of this mode share one
+        //              reference, so their off-diagonal tiles need no rescaling);
+        //   kRefBlock  else the block's middle token, under the same bound;
+        //   kRefEnds   else the block's two ends (its diagonal tile exact).
+        bool farB = false, farC = false;
 #pragma unroll
         for (int j = 0; j < TPP; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) far |= !(fabsf(gl[j][i] - mid[i]) <= kMidLimit);
-        const bool slow = __any(far) != 0;
+            for (int i = 0; i < 8; ++i) {
+                farB |= !(fabsf(gl[j][i] - mid[i]) <= kMidLimit);
+                farC |= !(fabsf(gl[j][i] - gM[i]) <= kMidLimit);
+            }
+        const int mode = __any(farC) == 0 ? kRefChunk : (__any(farB) == 0 ? kRefBlock : kRefEnds);
+        const bool slow = mode == kRefEnds;
         float rr[8], cr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            rr[i] = slow ? base[i] : mid[i];
-            cr[i] = slow ? base[i] + wtot[i] : mid[i];
+            const float m = mode == kRefChunk ? gM[i] : mid[i];
+            rr[i] = slow ? base[i] : m;
+            cr[i] = slow ? base[i] + wtot[i] : m;
         }
         if (lane < CO) {
 #pragma unroll
@@ -374,10 +402,16 @@ struct Producer {
                 *reinterpret_cast<floatx4*>(rec + R::G + 4 * grp_ch(co, 4)) = e1;
             }
         }
-        if (lane == 0) sFl()[wave] = slow;
-        // ---------------- operands: A/P rows and cols, E_s^T, Q_s fragments, X^T
+        if (lane == 0) sFl()[wave] = mode;
+        // ---------------- operands: A/P rows and cols, E_s^T, Kh^T, Q_s fragments, X^T
         {
-            _Float16 et[8][TPP];
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            // Kh = k e^{g_C - g} = (k e^{cr - g}) e^{g_C - cr}: both factors <= 1 or
+            // within e^{kMidLimit}, their product <= 1
+            float fK[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fK[i] = __builtin_amdgcn_exp2f(gC[i] - cr[i]);
+            h2 et[8], kt[8];   // E_s^T and Kh^T of a token pair, stored once both are formed
             const int kq = co >> 2, gq = co & 3;
 #pragma unroll
             for (int j = 0; j < TPP; ++j) {
@@ -399,7 +433,8 @@ struct Producer {
                     qq[i >> 2][i & 3] = (_Float16)(q8[i] * er);
                     kk[i >> 2][i & 3] = (_Float16)(k8[i] * ec);
                     qs[i] = (_Float16)(q8[i] * es);
-                    et[i][j] = (_Float16)(bk * es);
+                    et[i][j & 1] = (_Float16)(bk * es);
+                    kt[i][j & 1] = (_Float16)(k8[i] * (ec * fK[i]));
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -410,17 +445,14 @@ struct Producer {
                 }
                 // Q_s straight to its fragment: row t, K step kq, lane (t & 15) + 16 gq
                 *reinterpret_cast<half8*>(rec + R::Q + ((size_t)((t >> 4) * NKK + kq) * 64 + (t & 15) + 16 * gq) * 16) = qs;
-            }
+                if (j & 1) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < TPP; j += 2) {
-                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                    h2 v;
-                    v[0] = et[i][j];
-                    v[1] = et[i][j + 1];
-                    *reinterpret_cast<h2*>(sEt() + grp_ch(co, i) * LDT2 + part * TPP + j) = v;
+                    for (int i = 0; i < 8; ++i) {
+                        *reinterpret_cast<h2*>(sEt() + grp_ch(co, i) * LDT2 + t - 1) = et[i];
+                        *reinterpret_cast<h2*>(sKt() + grp_ch(co, i) * LDT2 + t - 1) = kt[i];
+                    }
                 }
+            }
             _Float16 xt[8][XTP];
 #pragma unroll
             for (int j = 0; j < XTP; ++j) {
@@ -431,7 +463,7 @@ struct Producer {
                     v8[2 * i + 1] = __uint_as_float(rv[j][i] & 0xffff0000u);
                 }
                 if (WS) {
-                    float wsv = __uint_as_float(rw[j][0] << 16);
+                    float wsv = __uint_as_float(j % 2 == 0 ? rws[j / 2] << 16 : rws[j / 2] & 0xffff0000u);
                     if (LG) wsv = gate_sigmoid(wsv);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = wsv;
@@ -479,7 +511,7 @@ struct Producer {
                 int t = task, mt = 0;
                 while (t > mt) { t -= mt + 1; ++mt; }
                 const int nt = t;
-                if (mt == nt && fl[mt]) continue;
+                if (mt == nt && fl[mt] == kRefEnds) continue;
                 const _Float16* xe = sE() + (16 * mt + r16) * LDE + 2 * g4;
                 const _Float16* xq = sQ() + (16 * mt + r16) * LDE + 2 * g4;
                 const _Float16* xk = sK() + (16 * nt + r16) * LDE + 2 * g4;
@@ -490,7 +522,7 @@ struct Producer {
                     fk[kk] = ld_h8(xk + 32 * kk);
                     fq[kk] = ld_h8(xq + 32 * kk);
                 }
-                if (mt != nt) {
+                if (mt != nt && !(fl[mt] == kRefChunk && fl[nt] == kRefChunk)) {
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) {
                         const int ch = 32 * kk + 2 * g4;
@@ -533,35 +565,34 @@ struct Producer {
         }
         lds_barrier();
         if (has_next) issue(p, ntok0, 1);
-        if (wave == 0) {
-            // diagonal 16x16 blocks of T: right-looking forward substitution in fp32,
-            // lane (blk, column jc), the columns of A streamed from the transposed copy
-            const int blk = lane >> 4, jc = lane & 15;
-            const float* ad = sAd() + blk * 16 * LDD;
-            floatx4 acol[2][4];
+        {
+            // diagonal block `wave` of T = (I + A)^-1 by forward substitution in fp32:
+            // lane (column jc, rows 4 rg .. 4 rg + 3) holds its rows' values of the
+            // column, and A's column m (rows 4 rg ..) comes from the transposed copy;
+            // step m takes x_m from the lane group holding row m and subtracts
+            // A[:, m] x_m (A is zero on and above the diagonal, so row m keeps x_m)
+            static_assert(NB == NW, "one diagonal block per wave");
+            const int jc = lane & 15, rg = lane >> 4;
+            const float* ad = sAd() + wave * 16 * LDD + 4 * rg;
+            floatx4 acol[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acol[0][q] = *reinterpret_cast<const floatx4*>(ad + 4 * q);
-            float x[16];
+            for (int m = 0; m < 16; ++m) acol[m] = *reinterpret_cast<const floatx4*>(ad + m * LDD);
+            floatx4 x;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+            for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == jc) ? 1.f : 0.f;
 #pragma unroll
             for (int m = 0; m < 15; ++m) {
-                if (m + 1 < 15) {
+                const float xm = __shfl(x[m & 3], jc + 16 * (m >> 2));
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acol[(m + 1) & 1][q] = *reinterpret_cast<const floatx4*>(ad + (m + 1) * LDD + 4 * q);
-                }
-                const float xm = x[m];
-#pragma unroll
-                for (int r = m + 1; r < 16; ++r) x[r] -= acol[m & 1][r >> 2][r & 3] * xm;
+                for (int i = 0; i < 4; ++i) x[i] -= acol[m][i] * xm;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sT()[(16 * blk + r) * LDT + 16 * blk + jc] = (_Float16)x[r];
-        } else {
-            // meanwhile: fragments of P (K = tokens) and Kh^T (K = tokens), the latter
-            // from the col operands rescaled to the chunk end: Kh = K_col e^{g_C - cr}
+            for (int i = 0; i < 4; ++i) sT()[(16 * wave + 4 * rg + i) * LDT + 16 * wave + jc] = (_Float16)x[i];
+        }
+        {
+            // fragments of P and Kh^T (both K = tokens) from their LDS rows
             constexpr int NPB = NB * (C / 32), NKB = (DK / 16) * (C / 32);
-            for (int task = wave - 1; task < NPB + NKB; task += NW - 1) {
+            for (int task = wave; task < NPB + NKB; task += NW) {
                 if (task < NPB) {
                     const int rt = task / (C / 32), kk = task % (C / 32);
                     const _Float16* src = sP() + (16 * rt + r16) * LDT + 32 * kk + g4;
@@ -569,19 +600,9 @@ struct Producer {
                         cat8(ld_h4(src), ld_h4(src + 16));
                 } else {
                     const int tk = task - NPB, mt = tk / (C / 32), kk = tk % (C / 32);
-                    const int ch = 16 * mt + r16;
-                    const _Float16* src = sK() + (32 * kk + g4) * LDE + ch;
-                    const float gc = ref[8 * DK + ch];
-                    const float f0 = __builtin_amdgcn_exp2f(gc - ref[(4 + 2 * kk) * DK + ch]);
-                    const float f1 = __builtin_amdgcn_exp2f(gc - ref[(4 + 2 * kk + 1) * DK + ch]);
-                    half4 a = ld_col4(src, LDE), b = ld_col4(src + 16 * LDE, LDE);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        a[i] = (_Float16)((float)a[i] * f0);
-                        b[i] = (_Float16)((float)b[i] * f1);
-                    }
+                    const _Float16* src = sKt() + (16 * mt + r16) * LDT2 + 32 * kk + g4;
                     *reinterpret_cast<half8*>(rec + R::K + ((size_t)(mt * (C / 32) + kk) * 64 + lane) * 16) =
-                        cat8(a, b);
+                        cat8(ld_h4w(src), ld_h4w(src + 16));
                 }
             }
         }
