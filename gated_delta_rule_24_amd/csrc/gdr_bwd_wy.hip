@@ -440,27 +440,19 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
 
     // ================= phase A: value columns 16 vt .. 16 vt + 15 (vt = wave), all tokens
     const int vt = wave, ct = wave;
-    // shared fragments into LDS (16-byte pieces, in record order)
-    {
-        constexpr int PW = C * D * 2 / 16, PT2 = 2 * C * C * 2 / 16, NPC = 2 * PW + PT2;
-        constexpr int PER = (NPC + 64 * NW - 1) / (64 * NW);
-        uint4 cp[PER];
+    // Every load of the phase is issued before the first wait: the shared
+    // fragments (copied into LDS, 16-byte pieces in record order) first, so
+    // that waiting for them leaves the later loads in flight.
+    constexpr int PW = C * D * 2 / 16, PT2 = 2 * C * C * 2 / 16, NPC = 2 * PW + PT2;
+    constexpr int PER = (NPC + 64 * NW - 1) / (64 * NW);
+    uint4 cp[PER];
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int pc = min(tid + 64 * NW * m, NPC - 1);
-            const size_t src = pc < PW ? R::W + (size_t)pc * 16
-                             : pc < 2 * PW ? R::KW + (size_t)(pc - PW) * 16 : R::PT + (size_t)(pc - 2 * PW) * 16;
-            cp[m] = *reinterpret_cast<const uint4*>(rec + src);
-        }
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int pc = tid + 64 * NW * m;
-            if (pc < NPC) *reinterpret_cast<uint4*>(smem + L::oFW + (size_t)pc * 16) = cp[m];
-        }
+    for (int m = 0; m < PER; ++m) {
+        const int pc = min(tid + 64 * NW * m, NPC - 1);
+        const size_t src = pc < PW ? R::W + (size_t)pc * 16
+                         : pc < 2 * PW ? R::KW + (size_t)(pc - PW) * 16 : R::PT + (size_t)(pc - 2 * PW) * 16;
+        cp[m] = *reinterpret_cast<const uint4*>(rec + src);
     }
-    auto lfrag = [&](size_t off) __attribute__((always_inline)) {
-        return *reinterpret_cast<const half8*>(smem + off + lo16);
-    };
     // inputs needed late in this phase: v and w for dv, dw; dO
     uint2 vr[NB], wr[NB], dor[NB];
 #pragma unroll
@@ -483,6 +475,14 @@ __global__ __launch_bounds__(D * 4, 1) void wgrad_kernel(BwdParams p, const unsi
         fsa[kk] = frag(sfr, SFB::block(vt, kk));
         fda[kk] = frag(dfr, SFB::block(vt, kk));
     }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int pc = tid + 64 * NW * m;
+        if (NPC % (64 * NW) == 0 || pc < NPC) *reinterpret_cast<uint4*>(smem + L::oFW + (size_t)pc * 16) = cp[m];
+    }
+    auto lfrag = [&](size_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const half8*>(smem + off + lo16);
+    };
     lds_barrier();
     // Y = W S' and Z = Kh D over the channels
     floatx4 Y[NB], Z[NB];
