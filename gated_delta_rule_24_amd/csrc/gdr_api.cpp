@@ -119,7 +119,7 @@ size_t gdr_chunk_fwd_varlen_workspace_bytes(int nseq, int H, int T, int d_k, int
                                             uint32_t flags) {
     if (nseq < 1 || H < 1 || T < 0 || (long long)nseq * H > (1LL << 28)) return 0;
     if ((flags & ~kKnownFlags) || !gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return 0;
-    return gdr::fwd_wy_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    return gdr::fwd_fz_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
 }
 
 gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
@@ -139,7 +139,7 @@ gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
     if ((long long)nseq * H > (1LL << 28) || (long long)H * (T / 64 + nseq) > (1LL << 30))
         return GDR_ERR_INVALID_ARG;
     if (!gdr::fwd_wy_supported(d_k, d_v, 64, flags)) return GDR_ERR_UNSUPPORTED;
-    const size_t need = gdr::fwd_wy_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
+    const size_t need = gdr::fwd_fz_varlen_workspace_bytes(H, T, nseq, d_k, d_v);
     if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
     gdr_status ds = check_device();
     if (ds != GDR_OK) return ds;
@@ -149,10 +149,9 @@ gdr_status gdr_chunk_fwd_varlen(const void* q, const void* k, const void* v,
     p.S0 = S0; p.o = o; p.Sf = S_final; p.states = nullptr; p.state_frags = nullptr;
     p.cu_seqlens = cu_seqlens; p.chunk_off = nullptr; p.chunk_tab = nullptr; p.seq_order = nullptr; p.nseq = nseq;
     p.BH = H; p.T = T; p.flags = flags;
-    const hipError_t e = gdr::launch_fwd_wy_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream);
-    if (e != hipSuccess) return from_hip(e);
-    // sequences whose decay left the chunk kernels' operand range: token by token
-    return from_hip(gdr::launch_exact_fwd(p, d_k, d_v, (hipStream_t)stream));
+    // the producer over every packed chunk, then one chain per (sequence, head);
+    // their operands reference each block's own decay, so any decay gives values
+    return from_hip(gdr::launch_fwd_fz_varlen(p, d_k, d_v, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

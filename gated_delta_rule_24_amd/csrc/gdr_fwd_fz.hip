@@ -143,9 +143,14 @@ __device__ __forceinline__ int grp_ch(int co, int i) {
 struct NextItem {
     bool has;
     size_t tok0;
+    int len;           // tokens of the chunk (C but for a packed sequence's last chunk)
 };
 
-template <int DK, int DV, bool AS, bool LG>
+// VL: packed variable-length sequences; a chunk may hold fewer than C tokens
+// (a sequence's last one).  Its missing rows are loaded from its last token (in
+// bounds) and then zeroed (q, k, v) or given no decay (log alpha), so they add
+// nothing to A, P, W, U' or the chunk's decay.
+template <int DK, int DV, bool AS, bool LG, bool VL = false>
 struct Producer {
     using L = ProdLayout<DK, DV>;
     using R = RecF<DK, DV>;
@@ -160,6 +165,7 @@ struct Producer {
     // raw inputs of one chunk (issued one chunk ahead, in three groups)
     uint2 rq[TPP][2], rk[TPP][2], rb[TPP][2];
     uint32_t rbs[TPP / 2], rws[XTP / 2];   // b, w of one value per token: two tokens' bf16 per word
+    uint32_t rbv[VL ? TPP : 1], rwv[VL ? XTP : 1];   // VL: the same, one token per word
     floatx4 rla[TPP][2];
     u32x4 rv[XTP], rw[XTP];
 
@@ -207,14 +213,16 @@ struct Producer {
     // value per token come from k or v instead (same shape, never used).  The
     // loads then take no branch, so no loaded register is copied (a copy would
     // wait for every load in flight).
-    __device__ __forceinline__ void issue(const FwdParams& p, size_t tok0, int group) {
+    __device__ __forceinline__ void issue(const FwdParams& p, size_t tok0, int group, int len = C) {
+        const size_t tlast = tok0 + (size_t)(len - 1);     // VL: rows past it read this token
         const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.b);
         const uint16_t* bv = BS ? reinterpret_cast<const uint16_t*>(p.k) : bg;
         if (group < 2) {
             const int c0 = grp_ch(co, 0), c1 = grp_ch(co, 4);
 #pragma unroll
             for (int j = 0; j < TPP; ++j) {
-                const size_t t = tok0 + part * TPP + j;
+                size_t t = tok0 + part * TPP + j;
+                if (VL) t = t < tlast ? t : tlast;
                 const size_t ix = t * DK;
                 if (group == 0) {
                     const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + ix;
@@ -224,7 +232,8 @@ struct Producer {
                     rk[j][0] = *reinterpret_cast<const uint2*>(kg + c0);
                     rk[j][1] = *reinterpret_cast<const uint2*>(kg + c1);
                 } else {
-                    if (j % 2 == 0) rbs[j / 2] = *reinterpret_cast<const uint32_t*>(bg + t);
+                    if constexpr (VL) rbv[j] = bg[t];
+                    else if (j % 2 == 0) rbs[j / 2] = *reinterpret_cast<const uint32_t*>(bg + t);
                     rb[j][0] = *reinterpret_cast<const uint2*>(bv + ix + c0);
                     rb[j][1] = *reinterpret_cast<const uint2*>(bv + ix + c1);
                     if constexpr (AS) {
@@ -241,11 +250,13 @@ struct Producer {
             const uint16_t* wv = WS ? vg : wg;
 #pragma unroll
             for (int j = 0; j < XTP; ++j) {
-                const size_t t = tok0 + xpart * XTP + j;
+                size_t t = tok0 + xpart * XTP + j;
+                if (VL) t = t < tlast ? t : tlast;
                 const size_t ix = t * DV + 8 * vo;
                 rv[j] = *reinterpret_cast<const u32x4*>(vg + ix);
                 rw[j] = *reinterpret_cast<const u32x4*>(wv + ix);
-                if (j % 2 == 0) rws[j / 2] = *reinterpret_cast<const uint32_t*>(wg + t);
+                if constexpr (VL) rwv[j] = wg[t];
+                else if (j % 2 == 0) rws[j / 2] = *reinterpret_cast<const uint32_t*>(wg + t);
             }
         }
     }
@@ -262,7 +273,8 @@ struct Producer {
     }
     __device__ __forceinline__ void gate_b(int j, float (&b8)[8]) const {
         if (BS) {
-            float bs = __uint_as_float(j % 2 == 0 ? rbs[j / 2] << 16 : rbs[j / 2] & 0xffff0000u);
+            float bs = VL ? __uint_as_float(rbv[j] << 16)
+                          : __uint_as_float(j % 2 == 0 ? rbs[j / 2] << 16 : rbs[j / 2] & 0xffff0000u);
             if (LG) bs = gate_sigmoid(bs);
 #pragma unroll
             for (int i = 0; i < 8; ++i) b8[i] = bs;
@@ -281,9 +293,22 @@ struct Producer {
     // hook.before() just before it, hook.after() just after it, returning the
     // next chunk (has, tok0).  Ends with an LDS barrier.
     template <typename Hook>
-    __device__ __forceinline__ void chunk(const FwdParams& p, unsigned char* rec, Hook& hook) {
+    __device__ __forceinline__ void chunk(const FwdParams& p, unsigned char* rec, Hook& hook, int len = C) {
         float* tot = sTot();
         float* ref = sRef();
+        if constexpr (VL) {
+            // rows past the chunk's tokens: q, k zero (v where it is used, log
+            // alpha below)
+#pragma unroll
+            for (int j = 0; j < TPP; ++j) {
+                const bool in = part * TPP + j < len;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    rq[j][h] = in ? rq[j][h] : make_uint2(0u, 0u);
+                    rk[j][h] = in ? rk[j][h] : make_uint2(0u, 0u);
+                }
+            }
+        }
         // ---------------- in-chunk prefix of log alpha, per channel (log2 units)
         if (LG) {
 #pragma unroll
@@ -293,6 +318,16 @@ struct Producer {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!AS || (hh == 0 && i == 0)) rla[j][hh][i] = gate_log_sigmoid(rla[j][hh][i]);
+        }
+        if constexpr (VL) {
+#pragma unroll
+            for (int j = 0; j < TPP; ++j) {
+                const bool in = part * TPP + j < len;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rla[j][hh][i] = in ? rla[j][hh][i] : 0.f;
+            }
         }
         float gl[TPP][8];     // prefix within the part, then the chunk-relative prefix
         float run[8];
@@ -457,13 +492,16 @@ struct Producer {
 #pragma unroll
             for (int j = 0; j < XTP; ++j) {
                 float v8[8], w8[8];
+                const bool vin = !VL || xpart * XTP + j < len;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    v8[2 * i] = __uint_as_float(rv[j][i] << 16);
-                    v8[2 * i + 1] = __uint_as_float(rv[j][i] & 0xffff0000u);
+                    const uint32_t u = vin ? rv[j][i] : 0u;
+                    v8[2 * i] = __uint_as_float(u << 16);
+                    v8[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
                 }
                 if (WS) {
-                    float wsv = __uint_as_float(j % 2 == 0 ? rws[j / 2] << 16 : rws[j / 2] & 0xffff0000u);
+                    float wsv = VL ? __uint_as_float(rwv[j] << 16)
+                                   : __uint_as_float(j % 2 == 0 ? rws[j / 2] << 16 : rws[j / 2] & 0xffff0000u);
                     if (LG) wsv = gate_sigmoid(wsv);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = wsv;
@@ -494,7 +532,7 @@ struct Producer {
         }
         if (slow) diag_exact(gl);
         // the next chunk's q and k load while this one is processed
-        if (has_next) issue(p, ntok0, 0);
+        if (has_next) issue(p, ntok0, 0, nx.len);
         lds_barrier();
 
         // ---------------- A = strict_lower(E K^T) (fp32), P = lower(Q K^T) (f16)
@@ -564,7 +602,7 @@ struct Producer {
             }
         }
         lds_barrier();
-        if (has_next) issue(p, ntok0, 1);
+        if (has_next) issue(p, ntok0, 1, nx.len);
         {
             // diagonal block `wave` of T = (I + A)^-1 by forward substitution in fp32:
             // lane (column jc, rows 4 rg .. 4 rg + 3) holds its rows' values of the
@@ -681,7 +719,7 @@ struct Producer {
             *reinterpret_cast<half8*>(rec + R::U + ((size_t)(nt * (C / 32) + kk) * 64 + lane) * 16) =
                 cat8(to_h4(acc[0]), to_h4(acc[1]));
         }
-        if (has_next) issue(p, ntok0, 2);
+        if (has_next) issue(p, ntok0, 2, nx.len);
         lds_barrier();
     }
 
@@ -836,12 +874,14 @@ struct Chain {
     // workgroup barrier per chunk: past it, chunk c's copies are in LDS, every
     // wave is done with chunk c - 1 (so its stage takes chunk c + 1's copies),
     // and chunk c + 1's readiness is in its slot.  Chunk c + 2's readiness is
-    // awaited while the compute waves work on chunk c.
+    // awaited while the compute waves work on chunk c.  bh indexes the state
+    // (S0, S_final); the last chunk stores its first last_rows output rows only;
+    // with NC = 0 the state passes through.
     template <typename Ready>
     __device__ __forceinline__ void run(const FwdParams& p, const unsigned char* rec0, size_t RB, int NC, int bh,
-                                        size_t tok_base, int colbase, Ready& rd) {
+                                        size_t tok_base, int colbase, Ready& rd, int last_rows = C) {
         int* s_ok = reinterpret_cast<int*>(smem + L::oOk);   // [2]: chunk x's readiness in slot x & 1
-        bool ok = NC > 0;
+        bool ok = true;
         if (NC > 0) {
             if (wave == kComputeWaves) {
                 rd.poll(0);
@@ -859,7 +899,7 @@ struct Chain {
             lds_barrier();
             ok = s_ok[0] != 0;
         }
-        if (wave < kComputeWaves) compute(p, rec0, NC, bh, tok_base, colbase, ok);
+        if (wave < kComputeWaves) compute(p, rec0, NC, bh, tok_base, colbase, ok, last_rows);
         else copy(rec0, RB, NC, ok, rd);
         lds_barrier();                                         // LDS free for the next chain
     }
@@ -867,7 +907,7 @@ struct Chain {
     template <typename Ready>
     __device__ __forceinline__ void copy(const unsigned char* rec0, size_t RB, int NC, bool ok, Ready& rd) {
         int* s_ok = reinterpret_cast<int*>(smem + L::oOk);
-        if (ok) fetch(rec0, 0);
+        if (ok && NC > 0) fetch(rec0, 0);
         for (int c = 0; c < NC && ok; ++c) {
             wait_vm<0>();                                      // this wave's copies of chunk c
             lds_barrier();
@@ -887,7 +927,7 @@ struct Chain {
     }
 
     __device__ __forceinline__ void compute(const FwdParams& p, const unsigned char* rec0, int NC, int bh,
-                                            size_t tok_base, int colbase, bool ok) {
+                                            size_t tok_base, int colbase, bool ok, int last_rows) {
         (void)rec0;
         const int col0 = colbase + 16 * SPW * wave;          // this wave's first column
         int* s_ok = reinterpret_cast<int*>(smem + L::oOk);
@@ -1023,10 +1063,12 @@ struct Chain {
                     for (int s = 0; s < SPW; ++s) O[s][rt] = mfma32(uf[s][kk], pf[rt][kk], O[s][rt]);
             // lane holds O[token 16 rt + n_l][columns 16 s + g4 .. + 3]
             const size_t tok0 = tok_base + (size_t)c * C;
+            const int rows = c + 1 < NC ? C : last_rows;
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) {
+                    if (16 * rt + n_l >= rows) continue;
                     const size_t base = (tok0 + 16 * rt + n_l) * DV + col0 + 16 * s + g4;
                     const floatx4 o = O[s][rt];
                     if (out_bf16) {
@@ -1081,7 +1123,56 @@ __global__ __launch_bounds__(256, 1) void prod_kernel(FwdParams p, unsigned char
         const int nx = idx + (int)gridDim.x;
         hook.nx.has = nx < total;
         hook.nx.tok0 = hook.nx.has ? tok_of(nx) : 0;
+        hook.nx.len = C;
         pr.chunk(p, ws + (size_t)idx * R::bytes, hook);
+    }
+}
+
+// Packed variable-length sequences (p.cu_seqlens and the prep arrays set; p.BH
+// = H heads of p.T packed tokens).  Work item = (head, chunk r of the head's
+// concatenated sequences), looked up in the chunk table; records numbered
+// head * (chunk count) + r, as the two-pass kernels number them.
+template <int DK, int DV, bool AS, bool LG>
+__global__ __launch_bounds__(256, 1) void prod_kernel_vl(FwdParams p, unsigned char* ws) {
+    using PR = Producer<DK, DV, AS, LG, true>;
+    using R = RecF<DK, DV>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int CN = p.chunk_off[p.nseq];
+    const int total = p.BH * CN;
+    int idx = blockIdx.x;
+    if (idx >= total) return;
+    PR pr;
+    pr.init(smem, p.flags);
+    const int2* tab = reinterpret_cast<const int2*>(p.chunk_tab);
+    auto item = [&](int i, size_t& t0, int& len) {
+        const int h = i / CN, r = i - h * CN;
+        const int2 e = tab[r];
+        t0 = (size_t)h * p.T + (size_t)e.x;
+        len = e.y;
+    };
+    {
+        size_t t0;
+        int len;
+        item(idx, t0, len);
+        pr.issue(p, t0, 0, len);
+        pr.issue(p, t0, 1, len);
+        pr.issue(p, t0, 2, len);
+    }
+    struct Hook {
+        NextItem nx;
+        __device__ void before() {}
+        __device__ NextItem after() { return nx; }
+    } hook;
+    for (; idx < total; idx += gridDim.x) {
+        const int nx = idx + (int)gridDim.x;
+        size_t t0;
+        int len;
+        item(idx, t0, len);
+        hook.nx.has = nx < total;
+        hook.nx.tok0 = 0;
+        hook.nx.len = C;
+        if (hook.nx.has) item(nx, hook.nx.tok0, hook.nx.len);
+        pr.chunk(p, ws + (size_t)idx * R::bytes, hook, len);
     }
 }
 
@@ -1100,6 +1191,28 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(FwdParams p, const unsign
         __device__ bool wait(int) { return true; }
     } rd;
     ch.run(p, ws + (size_t)bh * NC * R::bytes, R::bytes, NC, bh, (size_t)bh * p.T, (blockIdx.x % WPH) * kChainCols, rd);
+}
+
+// Packed sequences: one chain per (sequence, head) and column block, the
+// longest sequences first (p.seq_order); the state of sequence s on head h is
+// S0[s * H + h].
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void chain_kernel_vl(FwdParams p, const unsigned char* ws) {
+    using CH = Chain<DK, DV>;
+    using R = RecF<DK, DV>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int WPH = CH::L::WPH;
+    int blk = 0;
+    const int bh = wy::packed_chain(p.seq_order, p.BH, WPH, (int)blockIdx.x, (int)gridDim.x, blk);
+    const wy::PackedSpan sp = wy::packed_span(p.cu_seqlens, p.chunk_off, p.nseq, p.BH, p.T, bh);
+    CH ch;
+    ch.init(smem);
+    struct Always {
+        __device__ void poll(int) {}
+        __device__ bool wait(int) { return true; }
+    } rd;
+    const int last = sp.len - (sp.NC > 0 ? (sp.NC - 1) * C : 0);
+    ch.run(p, ws + sp.chunk0 * R::bytes, R::bytes, sp.NC, bh, sp.tok0, blk * kChainCols, rd, last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1246,6 +1359,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(FwdParams p, unsigned cha
             NextItem r;
             r.has = nx < total;
             r.tok0 = 0;
+            r.len = C;
             if (r.has) {
                 int h, c;
                 (*loc)(nx, h, c);
@@ -1371,7 +1485,72 @@ static hipError_t launch_modes(const FwdParams& p, void* ws, hipStream_t st) {
     return lg ? launch_pick<DK, DV, false, true>(p, ws, st) : launch_pick<DK, DV, false, false>(p, ws, st);
 }
 
+// packed sequences: the producer over every chunk, then the chains
+template <int DK, int DV, bool AS, bool LG>
+static hipError_t launch_vl_t(const FwdParams& p, void* records, hipStream_t st) {
+    using PL = ProdLayout<DK, DV>;
+    using CL = ChainLayout<DK, DV>;
+    auto kp = prod_kernel_vl<DK, DV, AS, LG>;
+    auto kc = chain_kernel_vl<DK, DV>;
+    static std::atomic<unsigned long long> done_p{0}, done_c{0};
+    hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kp), (int)PL::bytes, done_p);
+    if (e != hipSuccess) return e;
+    e = ensure_dyn_lds(reinterpret_cast<const void*>(kc), (int)CL::bytes, done_c);
+    if (e != hipSuccess) return e;
+    const Topology tp = topology();
+    hipLaunchKernelGGL(kp, dim3((unsigned)tp.ncu), dim3(256), PL::bytes, st, p,
+                       reinterpret_cast<unsigned char*>(records));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long chains = (long long)p.nseq * p.BH * CL::WPH;
+    hipLaunchKernelGGL(kc, dim3((unsigned)chains), dim3(256), CL::bytes, st, p,
+                       reinterpret_cast<const unsigned char*>(records));
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_vl_modes(const FwdParams& p, void* records, hipStream_t st) {
+    const bool as = (p.flags & GDR_ALPHA_SCALAR) != 0;
+    const bool lg = (p.flags & GDR_GATE_LOGITS) != 0;
+    if (as) return lg ? launch_vl_t<DK, DV, true, true>(p, records, st) : launch_vl_t<DK, DV, true, false>(p, records, st);
+    return lg ? launch_vl_t<DK, DV, false, true>(p, records, st) : launch_vl_t<DK, DV, false, false>(p, records, st);
+}
+
+template <int DK, int DV>
+static size_t vl_records_bytes(int H, long long T, int nseq) {
+    return (size_t)H * packed_max_chunks(T, nseq) * RecF<DK, DV>::bytes;
+}
+
 }  // namespace fz
+
+static size_t fz_vl_records_bytes(int H, long long T, int nseq, int dk, int dv) {
+    if (dk == 128 && dv == 128) return fz::vl_records_bytes<128, 128>(H, T, nseq);
+    if (dk == 64 && dv == 64) return fz::vl_records_bytes<64, 64>(H, T, nseq);
+    if (dk == 128 && dv == 64) return fz::vl_records_bytes<128, 64>(H, T, nseq);
+    if (dk == 64 && dv == 128) return fz::vl_records_bytes<64, 128>(H, T, nseq);
+    return 0;
+}
+
+size_t fwd_fz_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv) {
+    const size_t rb = fz_vl_records_bytes(H, T, nseq, dk, dv);
+    if (rb == 0 || H < 1 || nseq < 1 || T < 0) return 0;
+    return ((rb + 255) & ~size_t(255)) + packed_prep_bytes(T, nseq);
+}
+
+hipError_t launch_fwd_fz_varlen(const FwdParams& p0, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st) {
+    const size_t need = fwd_fz_varlen_workspace_bytes(p0.BH, p0.T, p0.nseq, dk, dv);
+    if (need == 0 || ws_bytes < need || !p0.cu_seqlens) return hipErrorInvalidValue;
+    FwdParams p = p0;
+    const size_t rb = (fz_vl_records_bytes(p.BH, p.T, p.nseq, dk, dv) + 255) & ~size_t(255);
+    unsigned char* prep = reinterpret_cast<unsigned char*>(ws) + rb;
+    hipError_t e = launch_packed_prep(p.cu_seqlens, p.nseq, p.T, prep, &p.chunk_off, &p.chunk_tab, &p.seq_order, st);
+    if (e != hipSuccess) return e;
+    if (dk == 128 && dv == 128) return fz::launch_vl_modes<128, 128>(p, ws, st);
+    if (dk == 64 && dv == 64) return fz::launch_vl_modes<64, 64>(p, ws, st);
+    if (dk == 128 && dv == 64) return fz::launch_vl_modes<128, 64>(p, ws, st);
+    if (dk == 64 && dv == 128) return fz::launch_vl_modes<64, 128>(p, ws, st);
+    return hipErrorInvalidValue;
+}
 
 size_t fwd_fz_workspace_bytes(int BH, int T, int dk, int dv) {
     size_t off = 0;

@@ -1107,14 +1107,6 @@ hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream
 }
 
 
-static size_t varlen_rec_bytes(int dk, int dv) {
-    if (dk == 128 && dv == 128) return wy::Rec<128, 128>::bytes;
-    if (dk == 64 && dv == 64) return wy::Rec<64, 64>::bytes;
-    if (dk == 128 && dv == 64) return wy::Rec<128, 64>::bytes;
-    if (dk == 64 && dv == 128) return wy::Rec<64, 128>::bytes;
-    return 0;
-}
-
 static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 size_t packed_max_chunks(long long T, int nseq) {
@@ -1145,12 +1137,6 @@ hipError_t launch_packed_prep(const int* cu_seqlens, int nseq, long long T, void
     return hipGetLastError();
 }
 
-size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv) {
-    const size_t rb = varlen_rec_bytes(dk, dv);
-    if (rb == 0 || H < 1 || nseq < 1 || T < 0) return 0;
-    return (size_t)H * packed_max_chunks(T, nseq) * rb + packed_prep_bytes(T, nseq);
-}
-
 hipError_t launch_fwd_wy_packed(const FwdParams& p, int dk, int dv, void* records, hipStream_t st,
                                 bool bwd_layouts, int passes) {
     if (!p.cu_seqlens || !p.chunk_off || !p.chunk_tab || !p.seq_order) return hipErrorInvalidValue;
@@ -1164,18 +1150,6 @@ hipError_t launch_fwd_wy_packed(const FwdParams& p, int dk, int dv, void* record
     if (dk == 128 && dv == 64) return wy::launch_modes<128, 64, false, true>(p, records, st, passes);
     if (dk == 64 && dv == 128) return wy::launch_modes<64, 128, false, true>(p, records, st, passes);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_fwd_wy_varlen(const FwdParams& p0, int dk, int dv, void* ws, size_t ws_bytes,
-                                hipStream_t st) {
-    const size_t need = fwd_wy_varlen_workspace_bytes(p0.BH, p0.T, p0.nseq, dk, dv);
-    if (need == 0 || ws_bytes < need || !p0.cu_seqlens) return hipErrorInvalidValue;
-    FwdParams p = p0;
-    const size_t rb = varlen_rec_bytes(dk, dv);
-    unsigned char* prep = reinterpret_cast<unsigned char*>(ws) + (size_t)p.BH * packed_max_chunks(p.T, p.nseq) * rb;
-    hipError_t e = launch_packed_prep(p.cu_seqlens, p.nseq, p.T, prep, &p.chunk_off, &p.chunk_tab, &p.seq_order, st);
-    if (e != hipSuccess) return e;
-    return launch_fwd_wy_packed(p, dk, dv, ws, st, false, kWyPass | kChainPass);
 }
 
 }  // namespace gdr

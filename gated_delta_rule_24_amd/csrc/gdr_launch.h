@@ -92,6 +92,10 @@ hipError_t launch_fwd_wy(const FwdParams& p, int dk, int dv, void* ws, hipStream
 // fwd_wy_supported without the backward layouts).
 size_t fwd_fz_workspace_bytes(int BH, int T, int dk, int dv);
 hipError_t launch_fwd_fz(const FwdParams& p, int dk, int dv, void* ws, hipStream_t st);
+// Packed variable-length sequences on the same producer and chain (two
+// kernels after the prep step): workspace = records, then the prep arrays.
+size_t fwd_fz_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
+hipError_t launch_fwd_fz_varlen(const FwdParams& p, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st);
 // Packed variable-length sequences.  Each head holds at most T/64 + nseq
 // chunks; records and fragments are numbered head * (chunk count) + chunk.
 // The prep step fills, in prep_bytes of device memory: the chunk offsets of
@@ -103,10 +107,6 @@ hipError_t launch_packed_prep(const int* cu_seqlens, int nseq, long long T, void
 // The two passes over packed sequences (p's prep pointers set).
 hipError_t launch_fwd_wy_packed(const FwdParams& p, int dk, int dv, void* records, hipStream_t st,
                                 bool bwd_layouts, int passes);
-// The whole packed forward: workspace = records, then the prep arrays.
-size_t fwd_wy_varlen_workspace_bytes(int H, long long T, int nseq, int dk, int dv);
-hipError_t launch_fwd_wy_varlen(const FwdParams& p, int dk, int dv, void* ws, size_t ws_bytes,
-                                hipStream_t st);
 
 struct BwdParams {
     const void* q;

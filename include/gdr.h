@@ -50,12 +50,13 @@
  *   in-chunk solve cancel by about two orders of magnitude, and such inputs
  *   need fp32 activations.
  * - Decay range: every call returns values for any decay an fp32 log_alpha
- *   can express.  The persistent forward references each 16-token block's
- *   decay so that no operand factor exceeds 1.  The other chunk kernels
- *   reference a chunk's decay to its end; a (sequence, head) whose in-chunk
- *   decay leaves their operand range (about 10 nats per chunk with f16
- *   operands) is recomputed token by token in fp32 by a follow-up kernel of
- *   the same call, which costs one small launch when no head needs it.
+ *   can express.  The forward with a workspace (fixed-length and packed)
+ *   references each 16-token block's decay so that no operand factor leaves
+ *   the f16 range.  The other chunk kernels reference a chunk's decay to its
+ *   end; a (sequence, head) whose in-chunk decay leaves their operand range
+ *   (about 10 nats per chunk with f16 operands) is recomputed token by token
+ *   in fp32 by a follow-up kernel of the same call, which costs one small
+ *   launch when no head needs it.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -191,8 +192,10 @@ gdr_status gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  *   o          : as gdr_chunk_fwd, [H, T, d_v]
  *   S_final    : fp32 [nseq, H, d_k, d_v]; NULL means not written; may alias S0
  *   workspace  : required, at least gdr_chunk_fwd_varlen_workspace_bytes()
- *                bytes (the two-pass path with chunks of 64; the tokens past a
- *                sequence's end in its last chunk are treated as absent).
+ *                bytes (chunks of 64: a record per chunk for the producer and
+ *                chain kernels of gdr_chunk_fwd, then the chunk tables; the
+ *                tokens past a sequence's end in its last chunk are treated as
+ *                absent).
  * Supported: bf16 activations, d_k and d_v in {64, 128}; nseq >= 1, H >= 1,
  * T >= 0.  Returns GDR_ERR_UNSUPPORTED otherwise.
  */

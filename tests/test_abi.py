@@ -181,12 +181,12 @@ def test_fwd_varlen_workspace_query():
     # so H * (T//64 + nseq) records cover any split of T tokens into nseq sequences;
     # then the nseq+1 chunk offsets, the (T//64 + nseq) x 2 chunk table and the
     # nseq-long sequence order (int32), each rounded up to 256 bytes
-    # the packed records: W, Kh^T, U', Q', P as f16 (d x 64 each, P 64 x 64) and
-    # the decay slot (4 d + 16 bytes rounded up to 256)
-    rec = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 768
+    # the packed records: W, Kh^T, U', Q_s, P as f16 (d x 64 each, P 64 x 64) and
+    # a 1 KiB decay slot, as for the fixed-length forward
+    rec = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 1024
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(3, 2, 200, 128, 128, 0) == 2 * (3 + 3) * rec + 768
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(64, 1, 0, 128, 128, 0) == 64 * rec + 1280
-    rec64 = 4 * 64 * 64 * 2 + 64 * 64 * 2 + 512
+    rec64 = 4 * 64 * 64 * 2 + 64 * 64 * 2 + 1024
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 4, 128, 64, 64, 0x1c) == 4 * 3 * rec64 + 768
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(0, 1, 64, 128, 128, 0) == 0
     assert lib.gdr_chunk_fwd_varlen_workspace_bytes(1, 1, 64, 128, 128, 0x1) == 0   # fp32
