@@ -446,6 +446,7 @@ def cpu_baseline(inp, min_seconds=10.0, max_passes=50, one_thread_seconds=4.0):
     sel = lambda x: x.reshape((FB * FH,) + x.shape[2:])
     args = [sel(a[n]) for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")]
     passes = 0
+    cores = oracle.num_threads()
     t0 = time.perf_counter()
     while True:
         oracle.fwd(*args)
@@ -463,7 +464,7 @@ def cpu_baseline(inp, min_seconds=10.0, max_passes=50, one_thread_seconds=4.0):
         dt1 = time.perf_counter() - t1
         if dt1 >= one_thread_seconds:
             break
-    return dict(value=passes * FB * FH * FT / dt, unit="tokens/s", cores=oracle.num_threads(),
+    return dict(value=passes * FB * FH * FT / dt, unit="tokens/s", cores=cores,
                 kind="oracle", cpu_model=cpu_model(), nproc=os.cpu_count(),
                 value_1thread=p1 * 2048 / dt1,
                 sample=f"full workload ({FB * FH} heads x {FT} tokens, d=128), {passes} passes of "

@@ -77,12 +77,16 @@ static void token_step(int dk, int dv, double* S, const double* q,
     }
 }
 
-static void set_threads(int nthreads)
+/* Threads for one call: nthreads if positive, else the OpenMP default.  The
+ * count goes into each loop's num_threads clause, so a call on one thread
+ * leaves later calls' default unchanged. */
+static int call_threads(int nthreads)
 {
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
     (void)nthreads;
+    return 1;
 #endif
 }
 
@@ -101,8 +105,9 @@ void oracle_fwd(int BH, int T, int dk, int dv,
                 const double* la, const double* b, const double* w,
                 const double* S0, double* o, double* S_final, int nthreads)
 {
-    set_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+    const int nt = call_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
     for (int h = 0; h < BH; ++h) {
         double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
         double* r = (double*)malloc(sizeof(double) * (size_t)dv);
@@ -126,8 +131,9 @@ void oracle_decode(int NH, int dk, int dv,
                    const double* la, const double* b, const double* w,
                    double* S, double* o, int nthreads)
 {
-    set_threads(nthreads);
-#pragma omp parallel for schedule(static)
+    const int nt = call_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for num_threads(nt) schedule(static)
     for (int h = 0; h < NH; ++h) {
         double* r = (double*)malloc(sizeof(double) * (size_t)dv);
         token_step(dk, dv, S + (size_t)h * dk * dv, q + (size_t)h * dk, k + (size_t)h * dk,
@@ -149,10 +155,11 @@ void oracle_bwd(int BH, int T, int dk, int dv,
                 double* dq, double* dk_, double* dv_, double* dla,
                 double* db, double* dw, double* dS0, int nthreads)
 {
-    set_threads(nthreads);
+    const int nt = call_threads(nthreads);
+    (void)nt;
     const size_t SS = (size_t)dk * dv;
     const int nseg = (T + SEG - 1) / SEG;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
     for (int h = 0; h < BH; ++h) {
         /* checkpoints: state before each segment */
         double* ck = (double*)malloc(sizeof(double) * SS * (size_t)nseg);
