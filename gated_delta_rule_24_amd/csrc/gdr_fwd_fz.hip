@@ -1471,34 +1471,9 @@ static hipError_t launch_split_t(const FwdParams& p, void* ws, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Whether the two-kernel form is expected to finish first.  The persistent
-// kernel chains at most CAP / WPH heads per XCD at once; with more heads per XCD
-// they run in batches while the producers have a quarter of the chip less,
-// whereas the two-kernel form runs every chain at once once all chunks exist.
-// Cycle costs per chunk measured on MI355X: a chain step 5.1k in the persistent
-// kernel and 4.8k alone, a producer chunk about 25k with a decay per channel
-// and 21k with one per token.  Both forms give the same results bit for bit.
-static bool split_expected_faster(const FwdParams& p, int WPH, bool as) {
-    const Topology tp = topology();
-    const double NC = (double)(p.T / C), BH = (double)p.BH;
-    const int cap = ((tp.ncu / tp.nx) / 4 > 0 ? (tp.ncu / tp.nx) / 4 : 1) / WPH > 0
-                        ? ((tp.ncu / tp.nx) / 4 > 0 ? (tp.ncu / tp.nx) / 4 : 1) / WPH : 1;
-    const int nh = (p.BH + tp.nx - 1) / tp.nx;               // heads of the busiest XCD
-    const int gens = (nh + cap - 1) / cap;
-    const int chain_cus = tp.nx * (nh < cap ? nh : cap) * WPH;
-    if (chain_cus >= tp.ncu) return true;
-    const double cp = as ? 21.0 : 25.0;
-    const double fused_chain = gens * NC * 5.1, fused_prod = BH * NC * cp / (tp.ncu - chain_cus);
-    const double fused = fused_chain > fused_prod ? fused_chain : fused_prod;
-    const double rounds = (double)((p.BH * WPH + tp.ncu - 1) / tp.ncu);
-    const double split = BH * NC * cp / tp.ncu + rounds * NC * 4.8;
-    return split < fused;
-}
-
 template <int DK, int DV, bool AS, bool LG>
 static hipError_t launch_pick(const FwdParams& p, void* ws, hipStream_t st) {
-    if ((p.flags & GDR_FWD_SPLIT) || split_expected_faster(p, ChainLayout<DK, DV>::WPH, AS))
-        return launch_split_t<DK, DV, AS, LG>(p, ws, st);
+    if (p.flags & GDR_FWD_SPLIT) return launch_split_t<DK, DV, AS, LG>(p, ws, st);
     return launch_t<DK, DV, AS, LG>(p, ws, st);
 }
 

@@ -90,10 +90,7 @@ typedef enum gdr_status {
 #define GDR_FWD_SPLIT     0x80u  /* forward with a workspace: run the chunk producer and
                                     the state chains as two kernels, one after the
                                     other, instead of one persistent kernel (same
-                                    results bit for bit).  Without the flag the
-                                    library picks the two kernels itself where it
-                                    expects them to finish first (many heads of
-                                    short sequences); the flag forces them.       */
+                                    results bit for bit; for testing)               */
 #define GDR_GATE_LOGITS   0x40u  /* log_alpha, b and w hold logits: the kernels use
                                     log alpha = log(sigmoid(log_alpha)), b = sigmoid(b),
                                     w = sigmoid(w) in fp32 (the token mixer's gating,

@@ -297,10 +297,9 @@ def test_strong_decay_leaves_other_heads_to_the_chunk_kernel():
     ("d64", dict(B=3, H=3, T=384, dk=64, dv=64, alpha_mode="scalar")),
     ("d128x64", dict(B=1, H=9, T=256, dk=128, dv=64, b_mode="scalar", w_mode="scalar", tied=True)),
     ("d64x128_strong", dict(B=1, H=2, T=256, dk=64, dv=128, decay_scale=2.0)),
-    # 64 heads of 24 chunks: two batches of chained heads per XCD, the producers
-    # following the batches (a shape for which the library keeps the persistent
-    # kernel; with many more heads of short sequences it runs the two kernels)
-    ("two_batches", dict(B=4, H=16, T=1536, dk=128, dv=128)),
+    # 80 heads of 24 chunks: three batches of chained heads per XCD, the
+    # producers following the batches
+    ("three_batches", dict(B=4, H=20, T=1536, dk=128, dv=128)),
 ])
 def test_persistent_and_split_kernels_agree_bitwise(name, kw):
     """The persistent kernel (producers and chains side by side, records handed
