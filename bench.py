@@ -93,7 +93,8 @@ BWD_STATE_BYTES_PER_HEAD = 2 * FD * FD * 4
 FWD_KERNEL_SOURCES = ["gated_delta_rule_24_amd/csrc/gdr_fwd_fz.hip",
                       "gated_delta_rule_24_amd/csrc/gdr_wy.h",
                       "gated_delta_rule_24_amd/csrc/gdr_device.h",
-                      "gated_delta_rule_24_amd/csrc/gdr_launch.h"]
+                      "gated_delta_rule_24_amd/csrc/gdr_launch.h",
+                      "gated_delta_rule_24_amd/build.py"]   # the compiler flags
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_gdn2_B2H16T8192_traffic.md")
 
 
