@@ -313,6 +313,44 @@ def test_persistent_and_split_kernels_agree_bitwise(name, kw):
     _check(inp, o1, s1, 2e-2)
 
 
+@pytest.mark.parametrize("path", ["auto", "split", "fused"])
+def test_forward_replays_from_a_graph(path):
+    """The fixed-length forward captured into a graph (persistent kernel: the
+    flag-clearing kernel and the producer/chain kernel; or the two-kernel form;
+    or the single kernel without a workspace) replays to the eager result bit
+    for bit, on several replays with eager work and synchronisations between
+    them, and the eager result matches the oracle."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    inp = _case("graph_fwd", B=2, H=3, T=320, dk=128, dv=128)
+    d = to_dev(inp)
+
+    def run():
+        return gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"],
+                             chunk=64, path=path)
+    eager = run()
+    torch.cuda.synchronize()
+    _check(inp, eager[0], eager[1], 2e-2)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        x = torch.randn(1 << 20, device="cuda")
+        x.mul_(2.0)
+        captured[0].fill_(float("nan"))      # the replay must write every output again
+        captured[1].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(captured[0], eager[0]) and torch.equal(captured[1], eager[1]), rep
+
+
 def test_many_heads_take_several_chain_batches():
     """More heads than chain workgroups per XCD: the chains of an XCD run in
     batches, and the producers follow the batches."""
