@@ -77,6 +77,46 @@ def test_random_backward(seed):
     assert all(e <= tol for e in errs.values()), errs
 
 
+@pytest.mark.parametrize("seed", range(300, 312))
+def test_random_gate_ranges(seed):
+    """Random configurations as above with random decay strength (the
+    synthetic decay scale 0.05, 0.5, 2 or 20: from the workloads' mild decay to
+    chunks decaying by tens of nats, which the chunk kernels that reference a
+    chunk's end hand to the token-level recompute) and erase gates drawn up to
+    1 or 2: forward on a random path and backward, values against the oracle."""
+    import torch
+    import gated_delta_rule_24_amd as gdr
+    cfg = _config(seed)
+    r = np.random.default_rng([seed, 97])
+    cfg["decay_scale"] = float(r.choice([0.05, 0.5, 2.0, 20.0]))
+    cfg["gate_hi"] = float(r.choice([1.0, 2.0]))
+    path = ["auto", "fused", "split"][seed % 3]
+    print(f"random gate ranges seed={seed} path={path} {cfg}", flush=True)
+    inp = gs.make_inputs(seed=seed, with_dO=True, **cfg)
+    d = to_dev(inp)
+    tol = 1e-4 if cfg["act"] == "f32" else 2e-2
+    o, sf = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"],
+                          chunk=cfg["chunk"], path=path)
+    s0 = d["S0"] if d["S0"] is not None else torch.zeros((inp.B, inp.H, inp.dk, inp.dv), device="cuda")
+    g = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], s0, d["dO"], None,
+                      chunk=cfg["chunk"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_fwd(inp)
+    eo = rel_err(flat_heads(o.cpu().numpy(), inp.B, inp.H), o_ref)
+    es = rel_err(flat_heads(sf.cpu().numpy(), inp.B, inp.H), s_ref)
+    a = inp.arrays
+    flat = lambda x: None if x is None else x.reshape((inp.B * inp.H,) + x.shape[2:])
+    ref = oracle.bwd(*(flat(a[n]) for n in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO")))
+    for n, mode in (("dlog_alpha", inp.alpha_mode), ("db", inp.b_mode), ("dw", inp.w_mode)):
+        if mode == "scalar":
+            ref[n] = ref[n].sum(-1)
+    errs = {n: rel_err(flat_heads(g[n].cpu().numpy(), inp.B, inp.H) if n != "dS0"
+                       else g[n].cpu().numpy().reshape(ref[n].shape), ref[n]) for n in ref}
+    errs["o"], errs["S_final"] = eo, es
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol})", flush=True)
+    assert all(e <= tol for e in errs.values()), errs
+
+
 @pytest.mark.parametrize("seed", range(200, 208))
 def test_random_packed(seed):
     """Random length mixes (empty, short and multi-chunk documents), random
