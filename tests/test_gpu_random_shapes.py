@@ -121,6 +121,19 @@ def test_random_gate_ranges(seed):
 def test_random_packed(seed):
     """Random length mixes (empty, short and multi-chunk documents), random
     gate modes and head sizes, optionally gate logits: forward and backward."""
+    _packed_case(seed, strong=False)
+
+
+@pytest.mark.parametrize("seed", range(400, 408))
+def test_random_packed_gate_ranges(seed):
+    """As above with a random decay strength (synthetic decay scale 0.5, 2 or
+    20: the packed backward's records leave their range and its units go to
+    the token-level recompute, while the packed forward references each
+    chunk's start) and erase gates drawn up to 1 or 2, without gate logits."""
+    _packed_case(seed, strong=True)
+
+
+def _packed_case(seed, strong):
     import torch
     import gated_delta_rule_24_amd as gdr
     r = np.random.default_rng([seed, 98])
@@ -128,9 +141,12 @@ def test_random_packed(seed):
     lengths = [int(x) for x in r.choice([0, 1, 7, 63, 64, 65, 100, 200], size=nseq)]
     D = int(r.choice([64, 128]))
     H = int(r.integers(1, 4))
-    logits = bool(r.random() < 0.4)
+    logits = bool(r.random() < 0.4) and not strong
     modes = dict(alpha_mode=str(r.choice(["channel", "scalar"])), b_mode=str(r.choice(["channel", "scalar"])),
                  w_mode=str(r.choice(["channel", "scalar"])))
+    if strong:
+        modes["decay_scale"] = float(r.choice([0.5, 2.0, 20.0]))
+        modes["gate_hi"] = float(r.choice([1.0, 2.0]))
     print(f"random packed seed={seed} lengths={lengths} H={H} d={D} logits={logits} {modes}", flush=True)
     inp = gs.packed_inputs(lengths, H, D, D, seed=seed, with_dO=True, **modes)
     a = dict(inp.arrays)
