@@ -23,7 +23,10 @@
 // once for a clean unit, so on inputs within range these launches cost one
 // small kernel each.
 //
-// Layout of the state over a workgroup of 256 threads: a 16 x 16 grid of
+// The forward runs one wave per (unit, 8 value columns), the state's columns
+// being independent under the update (see exact_fwd_kernel).  The backward
+// keeps a unit in one workgroup, since its key-side gradients sum over all
+// columns.  Layout of the state over a backward workgroup of 256 threads: a 16 x 16 grid of
 // tiles of (d_k/16) x (d_v/16) elements; thread t owns tile row t >> 4 and
 // tile column t & 15, so a row sum over the columns is a 16-lane shuffle
 // reduction and a column sum over the rows is a shuffle over the wave's four
@@ -224,49 +227,108 @@ __device__ __forceinline__ float load_out(const void* o, size_t idx, bool bf16) 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+// One wave per (unit, FC value columns).  The update keeps the state's
+// columns apart (S1 = diag(a) S, r = S1^T e, S = S1 + k u^T and o = S^T q are
+// per column), so a unit's recompute splits over its value columns with no
+// sum across workgroups.  Lane (c, g) = (lane % FC, lane / FC) holds column
+// col0 + c over rows g RPL .. g RPL + RPL - 1; a sum over the rows is the
+// lane's own sum plus three shuffles across the row groups.  Each workgroup
+// checks the marker in its own first column (every column of a marked unit's
+// last row is NaN), so no workgroup reads a marker another one has rewritten.
+constexpr int FC = 8;                       // value columns per workgroup
+
 template <int DK, int DV, bool F32>
-__global__ __launch_bounds__(NT) void exact_fwd_kernel(FwdParams p, int units) {
-    constexpr int TR = DK / 16, TC = DV / 16;
-    __shared__ Stage<DK, DV> sm;
-    Tile<DK, DV> tl;
-    tl.init();
+__global__ __launch_bounds__(64) void exact_fwd_kernel(FwdParams p, long long items) {
+    constexpr int RG = 64 / FC, RPL = DK / RG, NG = DV / FC;
+    static_assert(DK % RG == 0 && DV % FC == 0, "lane layout");
+    __shared__ float sq[TB][DK], sk[TB][DK], sa[TB][DK], se[TB][DK], sx[TB][FC];
+    const int lane = threadIdx.x, c = lane % FC, g = lane / FC;
     const bool out_bf16 = (p.flags & GDR_OUT_BF16) != 0;
-    const int H = p.BH;
-    for (int un = blockIdx.x; un < units; un += gridDim.x) {
-        const UnitSpan us = unit_span(p.cu_seqlens, H, p.T, un);
+    const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
+    const bool lg = p.flags & GDR_GATE_LOGITS;
+    for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+        const int un = (int)(item / NG), grp = (int)(item % NG);
+        const int col = grp * FC + c;
+        const UnitSpan us = unit_span(p.cu_seqlens, p.BH, p.T, un);
         if (us.len <= 0) continue;
-        const float mark = load_out<F32>(p.o, (us.tok0 + us.len - 1) * DV, out_bf16);
+        const float mark = load_out<F32>(p.o, (us.tok0 + us.len - 1) * DV + (size_t)grp * FC, out_bf16);
         if (!__builtin_isnan(mark)) continue;
-        float S[TR][TC], u[TC];
-        load_state<DK, DV>(p.S0 ? p.S0 + (size_t)un * DK * DV : nullptr, S, tl);
-        int rb = 0;
+        float S[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+            S[r] = p.S0 ? p.S0[((size_t)un * DK + g * RPL + r) * DV + col] : 0.f;
+        // Token inputs of a block of TB tokens, loaded into registers one block
+        // ahead (all of a block's loads issued together, so one block waits for
+        // one load latency at most, behind the previous block's arithmetic).
+        // Lanes past the unit's end load its first token (in bounds, unused).
+        constexpr int NL = TB * DK / 64;
+        static_assert(TB * DK % 64 == 0 && TB * FC == 64, "staging layout");
+        float rq[NL], rk[NL], rl[NL], rbv[NL], rw, rv;
+        auto load_block = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < NL; ++m) {
+                const int idx = lane + 64 * m, j = idx / DK, i = idx % DK;
+                const size_t tt = us.tok0 + (t0 + j < us.len ? t0 + j : 0);
+                rq[m] = load_act1<F32>(p.q, tt * DK + i);
+                rk[m] = load_act1<F32>(p.k, tt * DK + i);
+                rl[m] = as ? p.la[tt] : p.la[tt * DK + i];
+                rbv[m] = bs ? load_act1<F32>(p.b, tt) : load_act1<F32>(p.b, tt * DK + i);
+            }
+            const int j = lane / FC, cl = grp * FC + lane % FC;
+            const size_t tt = us.tok0 + (t0 + j < us.len ? t0 + j : 0);
+            rw = wsc ? load_act1<F32>(p.w, tt) : load_act1<F32>(p.w, tt * DV + cl);
+            rv = load_act1<F32>(p.v, tt * DV + cl);
+        };
+        load_block(0);
         for (int t0 = 0; t0 < us.len; t0 += TB) {
             const int n = us.len - t0 < TB ? us.len - t0 : TB;
             __syncthreads();
-            stage_tokens<DK, DV, F32>(sm, p.q, p.k, p.v, p.la, p.b, p.w, nullptr, us.tok0 + t0, n, p.flags);
-            __syncthreads();
-            for (int j = 0; j < n; ++j) {
-                step<DK, DV>(tl, sm, j, S, u, rb);
-                float part[TC];
+            // a = alpha, e = b⊙k; this workgroup's columns of x = w⊙v
 #pragma unroll
-                for (int c = 0; c < TC; ++c) {
-                    part[c] = 0.f;
-#pragma unroll
-                    for (int r = 0; r < TR; ++r) part[c] += S[r][c] * sm.q[j][tl.row(r)];
+            for (int m = 0; m < NL; ++m) {
+                const int idx = lane + 64 * m, j = idx / DK, i = idx % DK;
+                float l = rl[m], bb = rbv[m];
+                if (lg) {
+                    l = gate_log_sigmoid(l);
+                    bb = gate_sigmoid(bb);
                 }
-                tl.colsum(sm, part, rb);
-                if (tl.tr == 0) {
-                    const size_t base = (us.tok0 + t0 + j) * DV;
+                sq[j][i] = rq[m];
+                sk[j][i] = rk[m];
+                sa[j][i] = __expf(l);
+                se[j][i] = bb * rk[m];
+            }
+            sx[lane / FC][lane % FC] = (lg ? gate_sigmoid(rw) : rw) * rv;
+            __syncthreads();
+            if (t0 + TB < us.len) load_block(t0 + TB);
+            for (int j = 0; j < n; ++j) {
+                float r = 0.f;
 #pragma unroll
-                    for (int c = 0; c < TC; ++c) {
-                        if (out_bf16) reinterpret_cast<uint16_t*>(p.o)[base + tl.col(c)] = f32_to_bf16(part[c]);
-                        else reinterpret_cast<float*>(p.o)[base + tl.col(c)] = part[c];
-                    }
+                for (int i = 0; i < RPL; ++i) {
+                    S[i] *= sa[j][g * RPL + i];
+                    r += S[i] * se[j][g * RPL + i];
+                }
+#pragma unroll
+                for (int m = FC; m < 64; m *= 2) r += __shfl_xor(r, m);
+                const float u = sx[j][c] - r;
+                float o = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    S[i] += sk[j][g * RPL + i] * u;
+                    o += S[i] * sq[j][g * RPL + i];
+                }
+#pragma unroll
+                for (int m = FC; m < 64; m *= 2) o += __shfl_xor(o, m);
+                if (g == 0) {
+                    const size_t oi = (us.tok0 + t0 + j) * DV + col;
+                    if (out_bf16) reinterpret_cast<uint16_t*>(p.o)[oi] = f32_to_bf16(o);
+                    else reinterpret_cast<float*>(p.o)[oi] = o;
                 }
             }
         }
-        if (p.Sf) store_state<DK, DV>(p.Sf + (size_t)un * DK * DV, S, tl);
-        __syncthreads();
+        if (p.Sf) {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) p.Sf[((size_t)un * DK + g * RPL + r) * DV + col] = S[r];
+        }
     }
 }
 
@@ -479,9 +541,10 @@ __global__ __launch_bounds__(NT) void exact_bwd_kernel(BwdParams p, int units, f
 
 template <int DK, int DV>
 static hipError_t fwd_t(const FwdParams& p, int units, hipStream_t st) {
-    const unsigned grid = (unsigned)(units < 2048 ? units : 2048);
-    if (p.flags & GDR_ACT_F32) hipLaunchKernelGGL((exact_fwd_kernel<DK, DV, true>), dim3(grid), dim3(NT), 0, st, p, units);
-    else hipLaunchKernelGGL((exact_fwd_kernel<DK, DV, false>), dim3(grid), dim3(NT), 0, st, p, units);
+    const long long items = (long long)units * (DV / FC);
+    const unsigned grid = (unsigned)(items < 8192 ? items : 8192);
+    if (p.flags & GDR_ACT_F32) hipLaunchKernelGGL((exact_fwd_kernel<DK, DV, true>), dim3(grid), dim3(64), 0, st, p, items);
+    else hipLaunchKernelGGL((exact_fwd_kernel<DK, DV, false>), dim3(grid), dim3(64), 0, st, p, items);
     return hipGetLastError();
 }
 
