@@ -76,32 +76,56 @@ __device__ void stage_tokens(Stage<DK, DV>& sm, const void* q, const void* k, co
                              const void* b, const void* w, const void* dO, size_t tok, int n, uint32_t flags) {
     const bool as = flags & GDR_ALPHA_SCALAR, bs = flags & GDR_B_SCALAR, wsc = flags & GDR_W_SCALAR;
     const bool lg = flags & GDR_GATE_LOGITS;
-    for (int idx = threadIdx.x; idx < n * DK; idx += NT) {
-        const int j = idx / DK, i = idx % DK;
-        const size_t t = tok + j;
-        const float kk = load_act1<F32>(k, t * DK + i);
-        float l = as ? la[t] : la[t * DK + i];
-        float bb = bs ? load_act1<F32>(b, t) : load_act1<F32>(b, t * DK + i);
-        if (lg) {
-            l = gate_log_sigmoid(l);
-            bb = gate_sigmoid(bb);
-        }
-        sm.q[j][i] = load_act1<F32>(q, t * DK + i);
-        sm.k[j][i] = kk;
-        sm.a[j][i] = __expf(l);
-        sm.b[j][i] = bb;
-        sm.e[j][i] = bb * kk;
+    // Every load of the block first (a fixed count per thread, so they are
+    // issued together and the block waits for one load latency), then the
+    // stores.  Rows past the block's n tokens load its first token (in bounds)
+    // and are never read.
+    constexpr int MK = (TB * DK + NT - 1) / NT, MV = (TB * DV + NT - 1) / NT;
+    float rq[MK], rk[MK], rl[MK], rb[MK], rv[MV], rw[MV], rd[MV];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) {
+        const int idx = threadIdx.x + NT * m, j = idx / DK, i = idx % DK;
+        const size_t t = tok + (idx < TB * DK && j < n ? j : 0);
+        rk[m] = load_act1<F32>(k, t * DK + i);
+        rq[m] = load_act1<F32>(q, t * DK + i);
+        rl[m] = as ? la[t] : la[t * DK + i];
+        rb[m] = bs ? load_act1<F32>(b, t) : load_act1<F32>(b, t * DK + i);
     }
-    for (int idx = threadIdx.x; idx < n * DV; idx += NT) {
-        const int j = idx / DV, c = idx % DV;
-        const size_t t = tok + j;
-        const float vv = load_act1<F32>(v, t * DV + c);
-        float ww = wsc ? load_act1<F32>(w, t) : load_act1<F32>(w, t * DV + c);
-        if (lg) ww = gate_sigmoid(ww);
-        sm.v[j][c] = vv;
-        sm.w[j][c] = ww;
-        sm.x[j][c] = ww * vv;
-        if (dO) sm.dO[j][c] = load_act1<F32>(dO, t * DV + c);
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+        const int idx = threadIdx.x + NT * m, j = idx / DV, c = idx % DV;
+        const size_t t = tok + (idx < TB * DV && j < n ? j : 0);
+        rv[m] = load_act1<F32>(v, t * DV + c);
+        rw[m] = wsc ? load_act1<F32>(w, t) : load_act1<F32>(w, t * DV + c);
+        rd[m] = dO ? load_act1<F32>(dO, t * DV + c) : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < MK; ++m) {
+        const int idx = threadIdx.x + NT * m, j = idx / DK, i = idx % DK;
+        if (TB * DK % NT == 0 || idx < TB * DK) {
+            float l = rl[m], bb = rb[m];
+            if (lg) {
+                l = gate_log_sigmoid(l);
+                bb = gate_sigmoid(bb);
+            }
+            sm.q[j][i] = rq[m];
+            sm.k[j][i] = rk[m];
+            sm.a[j][i] = __expf(l);
+            sm.b[j][i] = bb;
+            sm.e[j][i] = bb * rk[m];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+        const int idx = threadIdx.x + NT * m, j = idx / DV, c = idx % DV;
+        if (TB * DV % NT == 0 || idx < TB * DV) {
+            float ww = rw[m];
+            if (lg) ww = gate_sigmoid(ww);
+            sm.v[j][c] = rv[m];
+            sm.w[j][c] = ww;
+            sm.x[j][c] = ww * rv[m];
+            if (dO) sm.dO[j][c] = rd[m];
+        }
     }
 }
 

@@ -58,7 +58,7 @@
  *   in fp32 by a follow-up kernel of the same call, which costs one small
  *   launch when no head needs it.  That recompute is sequential over a unit's
  *   tokens: a backward at B=1, H=32, T=16384, d=128 whose heads all leave the
- *   chunk-64 range takes about 260 ms instead of 2 ms.  Callers with such decay
+ *   chunk-64 range takes about 240 ms instead of 2 ms.  Callers with such decay
  *   should pass chunk 16 to gdr_chunk_bwd (about 10 nats per 16 tokens stay in
  *   range; the same backward then takes about 13 ms).
  */
