@@ -426,6 +426,43 @@ def bench_bwd(steps, warmup):
     return wall_ms, ev_ms, nbytes, step
 
 
+def bench_strong(steps, warmup):
+    """The backward workload (B=1, H=32, T=16384, d=128) with strong decay
+    (synthetic decay scale 0.5: chunks of 64 tokens decay by tens of nats, so
+    the chunk kernels that reference a chunk's end hand every head to the
+    token-level recompute): the backward at chunk 64 and chunk 16, and the
+    forward without a workspace.  Mean event ms per call of each."""
+    import torch
+    import gdr_synth as gs
+    import gated_delta_rule_24_amd as gdr
+    inp = gs.preset("gdn2_bwd", seed=0, decay_scale=0.5)
+    d = upload(inp)
+    f32 = torch.float32
+    shp = (BB, BH_, BT, FD)
+    g = {n: torch.empty(shp, dtype=f32, device="cuda") for n in ("dq", "dk", "dla", "db", "dv", "dw")}
+    dS0 = torch.empty((BB, BH_, FD, FD), dtype=f32, device="cuda")
+    flags = gdr.gate_flags(d["q"], d["log_alpha"], d["b"], d["w"])
+    out = {}
+    for chunk in (64, 16):
+        nbytes = gdr.gdr_chunk_bwd_workspace_bytes(BB, BH_, BT, FD, FD, chunk, flags)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+        def step():
+            gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"],
+                              None, g["dq"], g["dk"], g["dv"], g["dla"], g["db"], g["dw"], dS0,
+                              BB, BH_, BT, FD, FD, chunk, flags, ws, nbytes)
+        out[f"bwd_chunk{chunk}_ms"] = time_loop(step, steps, warmup)[1]
+        del ws
+    o = torch.empty(shp, dtype=f32, device="cuda")
+    Sf = torch.empty((BB, BH_, FD, FD), dtype=f32, device="cuda")
+
+    def fstep():
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], o, Sf,
+                          BB, BH_, BT, FD, FD, FC, flags, None, 0)
+    out["fwd_no_workspace_ms"] = time_loop(fstep, steps, warmup)[1]
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -480,7 +517,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["fwd", "gdn", "decode", "bwd", "copy", "varlen", "bwd_varlen",
-                                       "mixer"],
+                                       "mixer", "strong"],
                     default=None,
                     help="run one kernel only (for profiler runs); prints timings to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -519,6 +556,10 @@ def main():
         log(f"mixer prologue {pm * 1e3:.1f} us, epilogue {em * 1e3:.1f} us, q/k/v-only prologue "
             f"{qm * 1e3:.1f} us, forward on gate logits {fm * 1e3:.1f} us, prologue backward "
             f"{pbm * 1e3:.1f} us, epilogue backward {ebm * 1e3:.1f} us")
+        return
+    if args.only == "strong":
+        r = bench_strong(min(args.steps, 3), min(args.warmup, 1))
+        log("strong decay (decay scale 0.5): " + ", ".join(f"{k} {v:.2f}" for k, v in r.items()))
         return
     if args.only == "bwd_varlen":
         lengths, w, e, _ = bench_bwd_varlen(args.steps, args.warmup)
