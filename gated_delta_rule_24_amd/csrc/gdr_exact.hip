@@ -23,7 +23,7 @@
 // once for a clean unit, so on inputs within range these launches cost one
 // small kernel each.
 //
-// The forward runs one wave per (unit, 8 value columns), the state's columns
+// The forward runs one wave per (unit, 4 value columns), the state's columns
 // being independent under the update (see exact_fwd_kernel).  The backward
 // keeps a unit in one workgroup, since its key-side gradients sum over all
 // columns.  Layout of the state over a backward workgroup of 256 threads: a 16 x 16 grid of
@@ -256,16 +256,17 @@ __device__ __forceinline__ float load_out(const void* o, size_t idx, bool bf16) 
 // per column), so a unit's recompute splits over its value columns with no
 // sum across workgroups.  Lane (c, g) = (lane % FC, lane / FC) holds column
 // col0 + c over rows g RPL .. g RPL + RPL - 1; a sum over the rows is the
-// lane's own sum plus three shuffles across the row groups.  Each workgroup
+// lane's own sum plus four shuffles across the row groups.  Each workgroup
 // checks the marker in its own first column (every column of a marked unit's
 // last row is NaN), so no workgroup reads a marker another one has rewritten.
-constexpr int FC = 8;                       // value columns per workgroup
+constexpr int FC = 4;                       // value columns per workgroup
+constexpr int FTB = 64 / FC;                // tokens per staged block (one x value per lane)
 
 template <int DK, int DV, bool F32>
 __global__ __launch_bounds__(64) void exact_fwd_kernel(FwdParams p, long long items) {
     constexpr int RG = 64 / FC, RPL = DK / RG, NG = DV / FC;
     static_assert(DK % RG == 0 && DV % FC == 0, "lane layout");
-    __shared__ float sq[TB][DK], sk[TB][DK], sa[TB][DK], se[TB][DK], sx[TB][FC];
+    __shared__ float sq[FTB][DK], sk[FTB][DK], sa[FTB][DK], se[FTB][DK], sx[FTB][FC];
     const int lane = threadIdx.x, c = lane % FC, g = lane / FC;
     const bool out_bf16 = (p.flags & GDR_OUT_BF16) != 0;
     const bool as = p.flags & GDR_ALPHA_SCALAR, bs = p.flags & GDR_B_SCALAR, wsc = p.flags & GDR_W_SCALAR;
@@ -285,8 +286,8 @@ __global__ __launch_bounds__(64) void exact_fwd_kernel(FwdParams p, long long it
         // ahead (all of a block's loads issued together, so one block waits for
         // one load latency at most, behind the previous block's arithmetic).
         // Lanes past the unit's end load its first token (in bounds, unused).
-        constexpr int NL = TB * DK / 64;
-        static_assert(TB * DK % 64 == 0 && TB * FC == 64, "staging layout");
+        constexpr int NL = FTB * DK / 64;
+        static_assert(FTB * DK % 64 == 0 && FTB * FC == 64, "staging layout");
         float rq[NL], rk[NL], rl[NL], rbv[NL], rw, rv;
         auto load_block = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(64) void exact_fwd_kernel(FwdParams p, long long it
             rv = load_act1<F32>(p.v, tt * DV + cl);
         };
         load_block(0);
-        for (int t0 = 0; t0 < us.len; t0 += TB) {
-            const int n = us.len - t0 < TB ? us.len - t0 : TB;
+        for (int t0 = 0; t0 < us.len; t0 += FTB) {
+            const int n = us.len - t0 < FTB ? us.len - t0 : FTB;
             __syncthreads();
             // a = alpha, e = b⊙k; this workgroup's columns of x = w⊙v
 #pragma unroll
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(64) void exact_fwd_kernel(FwdParams p, long long it
             }
             sx[lane / FC][lane % FC] = (lg ? gate_sigmoid(rw) : rw) * rv;
             __syncthreads();
-            if (t0 + TB < us.len) load_block(t0 + TB);
+            if (t0 + FTB < us.len) load_block(t0 + FTB);
             for (int j = 0; j < n; ++j) {
                 float r = 0.f;
 #pragma unroll
