@@ -129,13 +129,19 @@ const char* gdr_status_string(gdr_status s);
  *                rounding for every chunk size.
  *   workspace  : optional device scratch owned by the caller, contents on
  *                entry ignored.  When it is non-NULL and
- *                gdr_chunk_fwd_workspace_bytes() is non-zero for the call, the
- *                two-pass path runs: every chunk's state-independent operands
- *                are first computed in parallel into the workspace, then a
- *                short per-head state chain consumes them.  workspace_bytes
- *                below the required size returns GDR_ERR_WORKSPACE.  With a
- *                NULL workspace (or a zero requirement) a single fused kernel
- *                runs.  Both paths give the same result up to rounding.
+ *                gdr_chunk_fwd_workspace_bytes() is non-zero for the call, a
+ *                persistent kernel runs (one workgroup per compute unit, after
+ *                a small kernel that clears the call's flags): producer
+ *                workgroups compute every chunk's state-independent operands
+ *                into the workspace while per-head state chains consume them,
+ *                each chunk handed over through a flag.  A chain waits for a
+ *                flag with a bounded spin (seconds); if the call's producers
+ *                cannot become resident meanwhile (another kernel holding the
+ *                compute units for that long), the chain stops and its head's
+ *                o and S_final are NaN.  workspace_bytes below the required
+ *                size returns GDR_ERR_WORKSPACE.  With a NULL workspace (or a
+ *                zero requirement) a single fused kernel runs.  Both paths
+ *                give the same result up to rounding.
  * Supported: d_k, d_v in {16, 32, 64, 128}; B*H >= 1; T >= 0 (T == 0 copies
  * S0 to S_final).  Returns GDR_ERR_UNSUPPORTED for other head sizes.
  */
